@@ -1,0 +1,199 @@
+"""Python binding of the attn_jvp C-ABI library (fused attention JVP, gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libattn_jvp.so``.  The library must have been built
+(``python -m attention_jvp_amd.build`` or ``__graft_entry__.build()``);
+importing this package does not load it, the first call does, and a missing
+library raises instead of falling back to anything else.
+
+Functions named like the C entry points take raw device pointers (ints) and
+return the C status; ``fwd`` is the torch-facing convenience that allocates
+the outputs with ``torch.empty`` and passes the current HIP stream.
+"""
+
+import ctypes
+import os
+
+__all__ = [
+    "ATTN_JVP_BF16", "ATTN_JVP_FP32", "AttnJvpError", "Layout", "Mask",
+    "attn_jvp_check", "attn_jvp_fwd", "attn_jvp_fwd_strided",
+    "attn_jvp_status_string", "attn_jvp_tile_shape", "attn_jvp_visible_tiles",
+    "exported_symbols", "fwd", "library_path", "load",
+]
+
+ATTN_JVP_BF16 = 0
+ATTN_JVP_FP32 = 1
+ATTN_JVP_MASK_FRAME_WINDOW = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libattn_jvp.so"
+
+
+class AttnJvpError(RuntimeError):
+    def __init__(self, status, what=""):
+        self.status = status
+        super().__init__(f"{what}: attn_jvp status {status} ({attn_jvp_status_string(status)})")
+
+
+class Mask(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "kind", "frames", "tokens_per_frame", "chunk_frames", "radius_chunks",
+        "anchor_first", "anchor_last", "anchor_queries_see_all")]
+
+    @classmethod
+    def frame_window(cls, frames, tokens_per_frame, chunk_frames, radius_chunks,
+                     anchor_first=1, anchor_last=1, anchor_queries_see_all=0):
+        return cls(ATTN_JVP_MASK_FRAME_WINDOW, frames, tokens_per_frame,
+                   chunk_frames, radius_chunks, int(anchor_first), int(anchor_last),
+                   int(anchor_queries_see_all))
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64 * 3) for n in ("q", "k", "v", "dq", "dk", "dv", "o", "dout")]
+
+
+_lib = None
+
+EXPORTS = ("attn_jvp_fwd", "attn_jvp_fwd_strided", "attn_jvp_check",
+           "attn_jvp_tile_shape", "attn_jvp_visible_tiles", "attn_jvp_status_string")
+
+
+def library_path():
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def load():
+    """Load the built library (once) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m attention_jvp_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, f32, i64p = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.POINTER(ctypes.c_int64)
+    ptrs10 = [vp] * 6 + [vp, vp, vp, vp]
+    lib.attn_jvp_fwd.argtypes = ptrs10 + [i32, i32, i32, i32, f32, i32, ctypes.POINTER(Mask), vp]
+    lib.attn_jvp_fwd.restype = i32
+    lib.attn_jvp_fwd_strided.argtypes = ptrs10 + [i32, i32, i32, i32, f32, i32,
+                                                  ctypes.POINTER(Layout), ctypes.POINTER(Mask), vp]
+    lib.attn_jvp_fwd_strided.restype = i32
+    lib.attn_jvp_check.argtypes = ptrs10 + [i32, i32, i32, i32, i32,
+                                            ctypes.POINTER(Layout), ctypes.POINTER(Mask)]
+    lib.attn_jvp_check.restype = i32
+    lib.attn_jvp_tile_shape.argtypes = [i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.attn_jvp_tile_shape.restype = i32
+    lib.attn_jvp_visible_tiles.argtypes = [i32, i32, i32, ctypes.POINTER(Mask), i64p]
+    lib.attn_jvp_visible_tiles.restype = i32
+    lib.attn_jvp_status_string.argtypes = [i32]
+    lib.attn_jvp_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def exported_symbols():
+    """Names of the C entry points the loaded library resolves."""
+    lib = load()
+    return [n for n in EXPORTS if hasattr(lib, n)]
+
+
+def _mask_ptr(mask):
+    if mask is None:
+        return None
+    if isinstance(mask, dict):
+        mask = Mask.frame_window(**mask)
+    return ctypes.pointer(mask)
+
+
+# ---- C entry points, same names, raw pointers -----------------------------
+
+def attn_jvp_fwd(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, B, H, N, d, scale, dtype,
+                 mask=None, stream=None):
+    return load().attn_jvp_fwd(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, B, H, N, d,
+                               scale, dtype, _mask_ptr(mask), stream)
+
+
+def attn_jvp_fwd_strided(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, B, H, N, d, scale,
+                         dtype, layout, mask=None, stream=None):
+    return load().attn_jvp_fwd_strided(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, B, H, N,
+                                       d, scale, dtype, ctypes.byref(layout),
+                                       _mask_ptr(mask), stream)
+
+
+def attn_jvp_check(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, B, H, N, d, dtype, layout,
+                   mask=None):
+    lay = None if layout is None else ctypes.byref(layout)
+    return load().attn_jvp_check(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, B, H, N, d,
+                                 dtype, lay, _mask_ptr(mask))
+
+
+def attn_jvp_tile_shape(dtype, d):
+    bm, bn = ctypes.c_int(), ctypes.c_int()
+    st = load().attn_jvp_tile_shape(dtype, d, ctypes.byref(bm), ctypes.byref(bn))
+    if st != 0:
+        raise AttnJvpError(st, "attn_jvp_tile_shape")
+    return bm.value, bn.value
+
+
+def attn_jvp_visible_tiles(N, dtype, d, mask=None):
+    bm, _ = attn_jvp_tile_shape(dtype, d)
+    out = (ctypes.c_int64 * ((N + bm - 1) // bm))()
+    st = load().attn_jvp_visible_tiles(N, dtype, d, _mask_ptr(mask), out)
+    if st != 0:
+        raise AttnJvpError(st, "attn_jvp_visible_tiles")
+    return list(out)
+
+
+def attn_jvp_status_string(status):
+    return load().attn_jvp_status_string(status).decode()
+
+
+# ---- torch convenience ----------------------------------------------------
+
+def _strides3(t):
+    s = t.stride()
+    if s[3] != 1:
+        raise ValueError("the last (head) dimension must be contiguous")
+    return (s[0], s[1], s[2])
+
+
+def layout_of(q, k, v, dq, dk, dv, o, do):
+    lay = Layout()
+    for name, t in zip(("q", "k", "v", "dq", "dk", "dv", "o", "dout"),
+                       (q, k, v, dq, dk, dv, o, do)):
+        getattr(lay, name)[:] = _strides3(t)
+    return lay
+
+
+def fwd(q, k, v, dq, dk, dv, scale=None, mask=None, out=None):
+    """(o, do, lse, dlse) for [B, H, N, d] CUDA tensors (bf16 or float32).
+
+    Tangents must have their primal's shape and strides.  ``mask`` is None or
+    a frame-window dict/Mask.  Outputs are allocated contiguous unless
+    ``out = (o, do, lse, dlse)`` is given.  Runs on the current stream.
+    """
+    import torch
+    dtypes = {torch.bfloat16: ATTN_JVP_BF16, torch.float32: ATTN_JVP_FP32}
+    if q.dtype not in dtypes:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    B, H, N, d = q.shape
+    if out is None:
+        o = torch.empty((B, H, N, d), device=q.device, dtype=q.dtype)
+        do = torch.empty_like(o)
+        lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
+        dlse = torch.empty_like(lse)
+    else:
+        o, do, lse, dlse = out
+    for t in (k, v, dq, dk, dv):
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v, dq, dk, dv must share shape, dtype and device")
+    lay = layout_of(q, k, v, dq, dk, dv, o, do)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = attn_jvp_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), dq.data_ptr(),
+                              dk.data_ptr(), dv.data_ptr(), o.data_ptr(), do.data_ptr(),
+                              lse.data_ptr(), dlse.data_ptr(), B, H, N, d,
+                              0.0 if scale is None else float(scale), dtypes[q.dtype],
+                              lay, mask, stream)
+    if st != 0:
+        raise AttnJvpError(st, "attn_jvp_fwd_strided")
+    return o, do, lse, dlse

@@ -1,0 +1,720 @@
+// Fused attention forward-mode derivative (JVP) for AMD gfx950 (MI355X).
+//
+// What is computed (page "带分数正则的一致性蒸馏", gitcode.csdn.net, section
+// 注意力): per query row, O = softmax(s Q K^T) V together with its tangent
+// dO = P dV + (P (.) dS) V - rowsum(P (.) dS) O, dS = s (dQ K^T + Q dK^T), the
+// natural-log row log-sum-exp and its tangent.  The pages stream K/V blocks
+// with an online max m, sum l, tangent sum r and accumulators O~, A~ = P~ dV,
+// B~ = H~ V (H~ = P~ (.) dS); only A~ + B~ is ever used, so this kernel keeps
+// a single tangent accumulator T~ = A~ + B~.
+//
+// gfx950 design (one workgroup = 4 waves = 128 query rows of one (b, h)):
+//   * every wave owns 32 query rows and computes the TRANSPOSED score tile
+//     S^T = K Q^T with v_mfma_f32_32x32x16_bf16: each lane then holds all of
+//     its query's scores for 16 of the 32 keys, so the row max needs one
+//     cross-lane step, the row sums stay lane-local until the epilogue, and
+//     the score fragment is already the B operand of the value products;
+//   * Q and dQ stay in registers (B operands) for the whole key loop;
+//   * K, dK are staged row-major in LDS (A operands of S^T and dS^T);
+//     V, dV are staged TRANSPOSED in LDS, with 4-key groups permuted inside
+//     each 16-key run so that a lane's 8 operand values are one 16-byte read;
+//   * O^T and T^T (= (A~ + B~)^T) accumulate in 32x32 fp32 fragments: every
+//     value a lane holds belongs to its own query, so the online rescale is
+//     one multiply by a per-lane factor;
+//   * exp2 domain for the scores (scale * log2 e folded into one FMA), the
+//     tangent stays in natural units;
+//   * workgroup ids are remapped so that all query blocks of one (b, h) land
+//     on the same XCD (dispatch round-robins consecutive ids over the 8 XCDs),
+//     keeping that head's K/V/dK/dV in one L2;
+//   * with a frame-window mask, each query block walks only the key-tile
+//     ranges some of its rows can see; element masks run on partial tiles.
+// float32 inputs use the same structure with v_mfma_f32_32x32x2_f32.
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "attn_jvp.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kWaveRows = 32;                  // query rows per wave
+constexpr int kBlockM = kWaves * kWaveRows;    // query rows per workgroup
+
+// ---------------------------------------------------------------------------
+// Element traits: operand fragment per lane for the 32x32 MFMA family.
+// ---------------------------------------------------------------------------
+template <typename T> struct Elem;
+
+template <> struct Elem<__bf16> {
+  using Frag = bf16x8;            // 8 bf16 along k per lane
+  static constexpr int KL = 8;    // k elements per lane
+  static constexpr int KI = 16;   // k per instruction (two lane halves)
+  __device__ static inline f32x16 mfma(Frag a, Frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline Frag pack(const f32x16 &x, int j) {
+    Frag f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = (__bf16)x[j * 8 + e];
+    return f;
+  }
+};
+
+template <> struct Elem<float> {
+  using Frag = float;
+  static constexpr int KL = 1;
+  static constexpr int KI = 2;
+  __device__ static inline f32x16 mfma(Frag a, Frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline Frag pack(const f32x16 &x, int j) { return x[j]; }
+};
+
+// ---------------------------------------------------------------------------
+// Frame-window mask (page "VDN-Minimax-H3 ... Stage A1", yfxerp.com).
+// ---------------------------------------------------------------------------
+struct MaskDev {
+  int kind;        // 0 none, 1 frame window
+  int frames, tpf, chunk, radius;
+  int first, last, see_all;
+  float inv_tpf, inv_chunk;
+};
+
+// floor(n / den) for 0 <= n < 2^24 from a float estimate and exact fix-up.
+__host__ __device__ inline int div_fix(int n, int den, float inv) {
+  int q = (int)((float)n * inv);
+  q -= (q * den > n);
+  q -= (q * den > n);
+  q += ((q + 1) * den <= n);
+  q += ((q + 1) * den <= n);
+  return q;
+}
+
+struct TileRanges {
+  int n;
+  int lo[3], hi[3];   // key-tile index ranges [lo, hi), ascending, disjoint
+};
+
+// Key-tile ranges that some query of rows [q_lo, q_hi) can see.
+__host__ __device__ inline TileRanges visible_tiles(const MaskDev &m, int q_lo,
+                                                    int q_hi, int N, int BN) {
+  TileRanges tr;
+  const int ntiles = (N + BN - 1) / BN;
+  tr.n = 1;
+  tr.lo[0] = 0;
+  tr.hi[0] = ntiles;
+  if (m.kind == 0) return tr;
+  const int T = m.tpf, C = m.chunk, F = m.frames, R = m.radius;
+  const int qf0 = q_lo / T, qf1 = (q_hi - 1) / T;
+  if (m.see_all && ((m.first && qf0 == 0) || (m.last && qf1 == F - 1))) return tr;
+  const int c0 = qf0 / C, c1 = qf1 / C;
+  int f_lo = (c0 - R) * C;
+  if (f_lo < 0) f_lo = 0;
+  long long f_hi_l = (long long)(c1 + R + 1) * C;
+  int f_hi = f_hi_l > F ? F : (int)f_hi_l;
+  // key intervals, then tiles
+  int klo[3], khi[3], n = 0;
+  if (m.first) { klo[n] = 0; khi[n] = T; ++n; }
+  klo[n] = f_lo * T; khi[n] = f_hi * T; ++n;
+  if (m.last) { klo[n] = (F - 1) * T; khi[n] = F * T; ++n; }
+  int tlo[3], thi[3];
+  for (int i = 0; i < n; ++i) {
+    tlo[i] = klo[i] / BN;
+    thi[i] = (khi[i] + BN - 1) / BN;
+  }
+  // intervals are already ascending by start; merge overlaps and contacts
+  tr.n = 0;
+  for (int i = 0; i < n; ++i) {
+    if (tr.n > 0 && tlo[i] <= tr.hi[tr.n - 1]) {
+      if (thi[i] > tr.hi[tr.n - 1]) tr.hi[tr.n - 1] = thi[i];
+    } else {
+      tr.lo[tr.n] = tlo[i];
+      tr.hi[tr.n] = thi[i];
+      ++tr.n;
+    }
+  }
+  return tr;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel parameters.
+// ---------------------------------------------------------------------------
+struct Params {
+  const void *q, *k, *v, *dq, *dk, *dv;
+  void *o, *dout;
+  float *lse, *dlse;
+  int64_t sq[3], sk[3], sv[3], so[3];   // (b, h, n) element strides
+  int B, H, N;
+  int nqb;                              // query blocks per (b, h)
+  float scale, scale_log2;
+  MaskDev mask;
+};
+
+__device__ inline int logical_block_id() {
+  // Dispatch places workgroup w on XCD (w mod 8).  Give each XCD a
+  // contiguous run of logical ids so a head's query blocks share one L2.
+  const int w = blockIdx.x, n = gridDim.x;
+  const int per = n / 8, rem = n % 8;
+  const int x = w % 8, local = w / 8;
+  return x * per + (x < rem ? x : rem) + local;
+}
+
+// Physical column of key `key` (0..BN-1) in a transposed V/dV row: 4-key
+// groups are permuted inside every 16-key run (group bits swapped) so that the
+// 8 keys one lane contributes to a k-step are contiguous.
+__device__ inline int vt_col(int key) {
+  const int g = key >> 2;
+  const int pg = (g & ~3) | ((g & 1) << 1) | ((g >> 1) & 1);
+  return (pg << 2) | (key & 3);
+}
+
+template <typename T, int D, int BN, bool MASKED>
+__global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
+  using E = Elem<T>;
+  using Frag = typename E::Frag;
+  constexpr int KL = E::KL;
+  constexpr int KI = E::KI;
+  constexpr int EV = 16 / sizeof(T);          // elements per 16-byte vector
+  constexpr int PAD = EV;                     // one 16-byte pad per LDS row
+  constexpr int LDK = D + PAD;                // K/dK LDS row length
+  constexpr int LDV = BN + PAD;               // V^T/dV^T LDS row length
+  constexpr int DS = D / KI;                  // k-steps over d
+  constexpr int NSB = BN / 32;                // 32-key sub-blocks per tile
+  constexpr int ND = D / 32;                  // 32-wide d blocks
+  constexpr int PS = 32 / KI;                 // k-steps per sub-block (P V)
+  constexpr int CPR = D / EV;                 // 16-byte chunks per row
+  static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
+
+  __shared__ __attribute__((aligned(16))) T smem[2 * BN * LDK + 2 * D * LDV];
+  T *Ks = smem;
+  T *dKs = Ks + BN * LDK;
+  T *Vt = dKs + BN * LDK;
+  T *dVt = Vt + D * LDV;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int qi = lane & 31;
+  const int hl = lane >> 5;
+
+  const int lid = logical_block_id();
+  const int bh = lid / p.nqb;
+  const int qb = lid - bh * p.nqb;
+  const int b = bh / p.H;
+  const int h = bh - b * p.H;
+  const int N = p.N;
+
+  const T *Q = (const T *)p.q + b * p.sq[0] + h * p.sq[1];
+  const T *dQ = (const T *)p.dq + b * p.sq[0] + h * p.sq[1];
+  const T *K = (const T *)p.k + b * p.sk[0] + h * p.sk[1];
+  const T *dK = (const T *)p.dk + b * p.sk[0] + h * p.sk[1];
+  const T *V = (const T *)p.v + b * p.sv[0] + h * p.sv[1];
+  const T *dV = (const T *)p.dv + b * p.sv[0] + h * p.sv[1];
+
+  const int q0 = qb * kBlockM;
+  const int qrow = q0 + wave * kWaveRows + qi;
+  const bool qvalid = qrow < N;
+
+  // ---- Q, dQ fragments (B operands of S^T = K Q^T), resident ----
+  Frag qf[DS], dqf[DS];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) {
+    if (qvalid) {
+      const int64_t off = (int64_t)qrow * p.sq[2] + s * KI + hl * KL;
+      qf[s] = *(const Frag *)(Q + off);
+      dqf[s] = *(const Frag *)(dQ + off);
+    } else {
+      qf[s] = Frag{};
+      dqf[s] = Frag{};
+    }
+  }
+
+  f32x16 oacc[ND], tacc[ND];
+#pragma unroll
+  for (int e = 0; e < ND; ++e) {
+    oacc[e] = f32x16{};
+    tacc[e] = f32x16{};
+  }
+  float m_run = -INFINITY;   // running max, log2 units
+  float l_run = 0.f;         // lane-partial running sum of P~
+  float r_run = 0.f;         // lane-partial running sum of H~
+
+  const float scale = p.scale;
+  const float c2 = p.scale_log2;
+
+  // query-side mask terms
+  int q_chunk = 0;
+  bool q_all = false;
+  if constexpr (MASKED) {
+    const int qf_ = div_fix(qvalid ? qrow : 0, p.mask.tpf, p.mask.inv_tpf);
+    q_chunk = div_fix(qf_, p.mask.chunk, p.mask.inv_chunk);
+    q_all = p.mask.see_all &&
+            ((p.mask.first && qf_ == 0) || (p.mask.last && qf_ == p.mask.frames - 1));
+  }
+
+  TileRanges tr;
+  if constexpr (MASKED) {
+    const int q_hi = (q0 + kBlockM < N) ? q0 + kBlockM : N;
+    tr = visible_tiles(p.mask, q0, q_hi, N, BN);
+  } else {
+    tr.n = 1;
+    tr.lo[0] = 0;
+    tr.hi[0] = (N + BN - 1) / BN;
+  }
+
+  // keys in [win_lo, win_hi) and the anchor frames are visible to every row
+  // of this query block; a tile inside one of them needs no element mask
+  int win_lo = 0, win_hi = 0;
+  if constexpr (MASKED) {
+    const int q_hi = (q0 + kBlockM < N) ? q0 + kBlockM : N;
+    const int c0 = (q0 / p.mask.tpf) / p.mask.chunk;
+    const int c1 = ((q_hi - 1) / p.mask.tpf) / p.mask.chunk;
+    int flo = (c1 - p.mask.radius) * p.mask.chunk;
+    long long fhi = (long long)(c0 + p.mask.radius + 1) * p.mask.chunk;
+    if (flo < 0) flo = 0;
+    if (fhi > p.mask.frames) fhi = p.mask.frames;
+    if (fhi > flo) {
+      win_lo = flo * p.mask.tpf;
+      win_hi = (int)fhi * p.mask.tpf;
+    }
+  }
+
+  for (int ri = 0; ri < tr.n; ++ri) {
+    for (int t = tr.lo[ri]; t < tr.hi[ri]; ++t) {
+      const int k0 = t * BN;
+
+      // ---- stage K, dK (row-major) and V, dV (transposed) into LDS ----
+      __syncthreads();   // previous tile fully consumed
+      constexpr int KCH = BN * CPR;            // 16-byte chunks per K tile
+#pragma unroll
+      for (int it = 0; it < (KCH + kThreads - 1) / kThreads; ++it) {
+        const int c = tid + it * kThreads;
+        if (KCH % kThreads != 0 && c >= KCH) break;
+        const int key = c / CPR;
+        const int col = (c - key * CPR) * EV;
+        uint4 kv = {0u, 0u, 0u, 0u}, dkv = {0u, 0u, 0u, 0u};
+        if (k0 + key < N) {
+          const int64_t off = (int64_t)(k0 + key) * p.sk[2] + col;
+          kv = *(const uint4 *)(K + off);
+          dkv = *(const uint4 *)(dK + off);
+        }
+        *(uint4 *)(Ks + key * LDK + col) = kv;
+        *(uint4 *)(dKs + key * LDK + col) = dkv;
+      }
+      constexpr int VCH = (BN / 4) * CPR;      // 4-key x 16-byte blocks
+#pragma unroll
+      for (int it = 0; it < (VCH + kThreads - 1) / kThreads; ++it) {
+        const int c = tid + it * kThreads;
+        if (VCH % kThreads != 0 && c >= VCH) break;
+        const int kg = c / CPR;
+        const int col = (c - kg * CPR) * EV;
+        uint4 vr[4], dvr[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int key = k0 + kg * 4 + j;
+          if (key < N) {
+            const int64_t off = (int64_t)key * p.sv[2] + col;
+            vr[j] = *(const uint4 *)(V + off);
+            dvr[j] = *(const uint4 *)(dV + off);
+          } else {
+            vr[j] = uint4{0u, 0u, 0u, 0u};
+            dvr[j] = uint4{0u, 0u, 0u, 0u};
+          }
+        }
+        const int pc = vt_col(kg * 4);
+        if constexpr (sizeof(T) == 2) {
+          const uint16_t *v16[4], *dv16[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            v16[j] = (const uint16_t *)&vr[j];
+            dv16[j] = (const uint16_t *)&dvr[j];
+          }
+#pragma unroll
+          for (int e = 0; e < EV; ++e) {
+            uint2 w, dw;
+            w.x = (uint32_t)v16[0][e] | ((uint32_t)v16[1][e] << 16);
+            w.y = (uint32_t)v16[2][e] | ((uint32_t)v16[3][e] << 16);
+            dw.x = (uint32_t)dv16[0][e] | ((uint32_t)dv16[1][e] << 16);
+            dw.y = (uint32_t)dv16[2][e] | ((uint32_t)dv16[3][e] << 16);
+            *(uint2 *)(Vt + (col + e) * LDV + pc) = w;
+            *(uint2 *)(dVt + (col + e) * LDV + pc) = dw;
+          }
+        } else {
+          const uint32_t *v32[4], *dv32[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            v32[j] = (const uint32_t *)&vr[j];
+            dv32[j] = (const uint32_t *)&dvr[j];
+          }
+#pragma unroll
+          for (int e = 0; e < EV; ++e) {
+            uint4 w = {v32[0][e], v32[1][e], v32[2][e], v32[3][e]};
+            uint4 dw = {dv32[0][e], dv32[1][e], dv32[2][e], dv32[3][e]};
+            *(uint4 *)(Vt + (col + e) * LDV + pc) = w;
+            *(uint4 *)(dVt + (col + e) * LDV + pc) = dw;
+          }
+        }
+      }
+      __syncthreads();
+
+      // ---- S^T and dS^T for every 32-key sub-block ----
+      f32x16 sacc[NSB], dsacc[NSB];
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) {
+        f32x16 s_ = f32x16{}, ds_ = f32x16{};
+        const T *krow = Ks + (sb * 32 + qi) * LDK + hl * KL;
+        const T *dkrow = dKs + (sb * 32 + qi) * LDK + hl * KL;
+#pragma unroll
+        for (int s = 0; s < DS; ++s) {
+          const Frag kf = *(const Frag *)(krow + s * KI);
+          const Frag dkf = *(const Frag *)(dkrow + s * KI);
+          s_ = E::mfma(kf, qf[s], s_);
+          ds_ = E::mfma(kf, dqf[s], ds_);
+          ds_ = E::mfma(dkf, qf[s], ds_);
+        }
+        sacc[sb] = s_;
+        dsacc[sb] = ds_;
+      }
+
+      // ---- masks: key tail and partial frame-window tiles ----
+      const bool tail = k0 + BN > N;
+      bool partial = false;
+      if constexpr (MASKED) {
+        const int k1 = k0 + BN;
+        const bool in_win = k0 >= win_lo && k1 <= win_hi;
+        const bool in_first = p.mask.first && k1 <= p.mask.tpf;
+        const bool in_last = p.mask.last && k0 >= (p.mask.frames - 1) * p.mask.tpf;
+        partial = !(in_win || in_first || in_last);
+      }
+      if (tail || partial) {
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + sb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+            bool vis = key < N;
+            if constexpr (MASKED) {
+              if (partial && vis && !q_all) {
+                const int kf_ = div_fix(key, p.mask.tpf, p.mask.inv_tpf);
+                const int kc = div_fix(kf_, p.mask.chunk, p.mask.inv_chunk);
+                const int dc = kc > q_chunk ? kc - q_chunk : q_chunk - kc;
+                vis = dc <= p.mask.radius || (p.mask.first && kf_ == 0) ||
+                      (p.mask.last && kf_ == p.mask.frames - 1);
+              }
+            }
+            if (!vis) {
+              sacc[sb][r] = -INFINITY;
+              dsacc[sb][r] = 0.f;
+            }
+          }
+        }
+      }
+
+      // ---- online softmax (log2 domain) ----
+      float mx = -INFINITY;
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx * c2);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      float lsum = 0.f, rsum = 0.f;
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[sb][r], c2, -m_use));
+          const float hv = pv * (dsacc[sb][r] * scale);
+          lsum += pv;
+          rsum += hv;
+          sacc[sb][r] = pv;
+          dsacc[sb][r] = hv;
+        }
+      }
+      l_run = fmaf(l_run, alpha, lsum);
+      r_run = fmaf(r_run, alpha, rsum);
+      m_run = m_new;
+#pragma unroll
+      for (int e = 0; e < ND; ++e) {
+        oacc[e] *= alpha;
+        tacc[e] *= alpha;
+      }
+
+      // ---- O^T += V^T P^T ; T^T += dV^T P^T + V^T H^T ----
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) {
+#pragma unroll
+        for (int j = 0; j < PS; ++j) {
+          const Frag pf = E::pack(sacc[sb], j);
+          const Frag hf = E::pack(dsacc[sb], j);
+          // register r = j*KL + i of lane half hl sits at physical column
+          // 16*(r/8) + 8*hl + r%8 of the 32-key sub-block
+          const int r0 = j * KL;
+          const int pc = sb * 32 + 16 * (r0 >> 3) + 8 * hl + (r0 & 7);
+#pragma unroll
+          for (int e = 0; e < ND; ++e) {
+            const int drow = e * 32 + qi;
+            const Frag vf = *(const Frag *)(Vt + drow * LDV + pc);
+            const Frag dvf = *(const Frag *)(dVt + drow * LDV + pc);
+            oacc[e] = E::mfma(vf, pf, oacc[e]);
+            tacc[e] = E::mfma(dvf, pf, tacc[e]);
+            tacc[e] = E::mfma(vf, hf, tacc[e]);
+          }
+        }
+      }
+    }
+  }
+
+  // ---- epilogue ----
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float r_tot = r_run + __shfl_xor(r_run, 32);
+  const bool empty = !(l_tot > 0.f);
+  const float inv = empty ? 0.f : 1.f / l_tot;
+  const float mu = r_tot * inv;
+  if (qvalid) {
+    T *O = (T *)p.o + b * p.so[0] + h * p.so[1] + (int64_t)qrow * p.so[2];
+    T *dO = (T *)p.dout + b * p.so[0] + h * p.so[1] + (int64_t)qrow * p.so[2];
+#pragma unroll
+    for (int e = 0; e < ND; ++e) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = e * 32 + 8 * g + 4 * hl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float o = oacc[e][4 * g + i] * inv;
+          const float dov = tacc[e][4 * g + i] * inv - mu * o;
+          O[d0 + i] = (T)o;
+          dO[d0 + i] = (T)dov;
+        }
+      }
+    }
+    if (hl == 0) {
+      const int64_t ro = (int64_t)bh * N + qrow;
+      p.lse[ro] = empty ? -INFINITY : (m_run + log2f(l_tot)) * 0.69314718055994530942f;
+      p.dlse[ro] = mu;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+constexpr int kBlockN = 64;
+
+struct Extent {
+  uintptr_t lo, hi;
+};
+
+Extent extent_of(const void *ptr, const int64_t s[3], int B, int H, int N, int d,
+                 int esize) {
+  const int64_t last = (int64_t)(B - 1) * s[0] + (int64_t)(H - 1) * s[1] +
+                       (int64_t)(N - 1) * s[2] + d;
+  return Extent{(uintptr_t)ptr, (uintptr_t)ptr + (uintptr_t)(last * esize)};
+}
+
+bool overlaps(Extent a, Extent b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool same3(const int64_t a[3], const int64_t b[3]) {
+  return a[0] == b[0] && a[1] == b[1] && a[2] == b[2];
+}
+
+int check_mask(const attn_jvp_mask *mask, int N) {
+  if (mask == nullptr || mask->kind == ATTN_JVP_MASK_NONE) return ATTN_JVP_OK;
+  if (mask->kind != ATTN_JVP_MASK_FRAME_WINDOW) return ATTN_JVP_EMASK;
+  if (mask->frames < 1 || mask->tokens_per_frame < 1 || mask->chunk_frames < 1 ||
+      mask->radius_chunks < 0)
+    return ATTN_JVP_EMASK;
+  if ((int64_t)mask->frames * mask->tokens_per_frame != N) return ATTN_JVP_EMASK;
+  if (N >= (1 << 24)) return ATTN_JVP_EMASK;   // frame arithmetic range
+  return ATTN_JVP_OK;
+}
+
+MaskDev to_dev(const attn_jvp_mask *mask) {
+  MaskDev m;
+  memset(&m, 0, sizeof(m));
+  if (mask == nullptr || mask->kind == ATTN_JVP_MASK_NONE) return m;
+  m.kind = 1;
+  m.frames = mask->frames;
+  m.tpf = mask->tokens_per_frame;
+  m.chunk = mask->chunk_frames;
+  // a radius of `frames` already reaches every chunk
+  m.radius = mask->radius_chunks > mask->frames ? mask->frames : mask->radius_chunks;
+  m.first = mask->anchor_first != 0;
+  m.last = mask->anchor_last != 0;
+  m.see_all = mask->anchor_queries_see_all != 0;
+  m.inv_tpf = 1.0f / (float)m.tpf;
+  m.inv_chunk = 1.0f / (float)m.chunk;
+  return m;
+}
+
+int check_args(const void *Q, const void *K, const void *V, const void *dQ,
+               const void *dK, const void *dV, void *O, void *dO, float *LSE,
+               float *dLSE, int B, int H, int N, int d, int dtype,
+               const attn_jvp_layout *L, const attn_jvp_mask *mask) {
+  if (!Q || !K || !V || !dQ || !dK || !dV || !O || !dO || !LSE || !dLSE || !L)
+    return ATTN_JVP_EINVAL;
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return ATTN_JVP_EINVAL;
+  if (dtype != ATTN_JVP_BF16 && dtype != ATTN_JVP_FP32) return ATTN_JVP_EINVAL;
+  if ((int64_t)B * H * ((N + kBlockM - 1) / kBlockM) > 0x7fffffffLL) return ATTN_JVP_EINVAL;
+  if (d != 64 && d != 128) return ATTN_JVP_EUNSUPPORTED;
+  if (dtype == ATTN_JVP_FP32 && d != 64) return ATTN_JVP_EUNSUPPORTED;
+  if (!same3(L->q, L->dq) || !same3(L->k, L->dk) || !same3(L->v, L->dv) ||
+      !same3(L->o, L->dout))
+    return ATTN_JVP_ESTRIDE;
+  const int esize = dtype == ATTN_JVP_BF16 ? 2 : 4;
+  const int64_t align = 16 / esize;
+  const int64_t *all[4] = {L->q, L->k, L->v, L->o};
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 3; ++j)
+      if (all[i][j] < 0 || all[i][j] % align != 0) return ATTN_JVP_ESTRIDE;
+  const void *ptrs[8] = {Q, K, V, dQ, dK, dV, O, dO};
+  for (int i = 0; i < 8; ++i)
+    if ((uintptr_t)ptrs[i] % 16 != 0) return ATTN_JVP_ESTRIDE;
+  if ((uintptr_t)LSE % 4 != 0 || (uintptr_t)dLSE % 4 != 0) return ATTN_JVP_ESTRIDE;
+  // outputs must not overlap inputs or each other
+  const Extent in[6] = {
+      extent_of(Q, L->q, B, H, N, d, esize),  extent_of(K, L->k, B, H, N, d, esize),
+      extent_of(V, L->v, B, H, N, d, esize),  extent_of(dQ, L->q, B, H, N, d, esize),
+      extent_of(dK, L->k, B, H, N, d, esize), extent_of(dV, L->v, B, H, N, d, esize)};
+  const int64_t rows = (int64_t)B * H * N;
+  const Extent out[4] = {extent_of(O, L->o, B, H, N, d, esize),
+                         extent_of(dO, L->o, B, H, N, d, esize),
+                         Extent{(uintptr_t)LSE, (uintptr_t)LSE + (uintptr_t)(rows * 4)},
+                         Extent{(uintptr_t)dLSE, (uintptr_t)dLSE + (uintptr_t)(rows * 4)}};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(out[i], in[j])) return ATTN_JVP_ESTRIDE;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(out[i], out[j])) return ATTN_JVP_ESTRIDE;
+  }
+  return check_mask(mask, N);
+}
+
+template <typename T, int D, bool MASKED>
+hipError_t launch(const Params &p, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((attn_jvp_kernel<T, D, kBlockN, MASKED>), dim3(grid),
+                     dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_m(const Params &p, int grid, hipStream_t stream) {
+  return p.mask.kind ? launch<T, D, true>(p, grid, stream)
+                     : launch<T, D, false>(p, grid, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_jvp_check(const void *Q, const void *K, const void *V, const void *dQ,
+                   const void *dK, const void *dV, void *O, void *dO, float *LSE,
+                   float *dLSE, int B, int H, int N, int d, int dtype,
+                   const attn_jvp_layout *layout, const attn_jvp_mask *mask) {
+  return check_args(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, B, H, N, d, dtype,
+                    layout, mask);
+}
+
+int attn_jvp_fwd_strided(const void *Q, const void *K, const void *V,
+                         const void *dQ, const void *dK, const void *dV, void *O,
+                         void *dO, float *LSE, float *dLSE, int B, int H, int N,
+                         int d, float scale, int dtype,
+                         const attn_jvp_layout *layout, const attn_jvp_mask *mask,
+                         void *stream) {
+  const int st = check_args(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, B, H, N, d,
+                            dtype, layout, mask);
+  if (st != ATTN_JVP_OK) return st;
+  Params p;
+  memset(&p, 0, sizeof(p));
+  p.q = Q; p.k = K; p.v = V; p.dq = dQ; p.dk = dK; p.dv = dV;
+  p.o = O; p.dout = dO; p.lse = LSE; p.dlse = dLSE;
+  for (int i = 0; i < 3; ++i) {
+    p.sq[i] = layout->q[i];
+    p.sk[i] = layout->k[i];
+    p.sv[i] = layout->v[i];
+    p.so[i] = layout->o[i];
+  }
+  p.B = B; p.H = H; p.N = N;
+  p.nqb = (N + kBlockM - 1) / kBlockM;
+  p.scale = (scale > 0.f && isfinite(scale)) ? scale : 1.0f / sqrtf((float)d);
+  p.scale_log2 = p.scale * 1.4426950408889634f;
+  p.mask = to_dev(mask);
+  const int grid = B * H * p.nqb;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t err;
+  if (dtype == ATTN_JVP_BF16)
+    err = d == 128 ? launch_m<__bf16, 128>(p, grid, s) : launch_m<__bf16, 64>(p, grid, s);
+  else
+    err = launch_m<float, 64>(p, grid, s);
+  return err == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_EHIP;
+}
+
+int attn_jvp_fwd(const void *Q, const void *K, const void *V, const void *dQ,
+                 const void *dK, const void *dV, void *O, void *dO, float *LSE,
+                 float *dLSE, int B, int H, int N, int d, float scale, int dtype,
+                 const attn_jvp_mask *mask, void *stream) {
+  attn_jvp_layout L;
+  const int64_t s[3] = {(int64_t)H * N * d, (int64_t)N * d, (int64_t)d};
+  for (int i = 0; i < 3; ++i) {
+    L.q[i] = L.k[i] = L.v[i] = L.dq[i] = L.dk[i] = L.dv[i] = L.o[i] = L.dout[i] = s[i];
+  }
+  return attn_jvp_fwd_strided(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, B, H, N, d,
+                              scale, dtype, &L, mask, stream);
+}
+
+int attn_jvp_tile_shape(int dtype, int d, int *block_m, int *block_n) {
+  if (!block_m || !block_n) return ATTN_JVP_EINVAL;
+  if (dtype != ATTN_JVP_BF16 && dtype != ATTN_JVP_FP32) return ATTN_JVP_EINVAL;
+  if (d != 64 && d != 128) return ATTN_JVP_EUNSUPPORTED;
+  if (dtype == ATTN_JVP_FP32 && d != 64) return ATTN_JVP_EUNSUPPORTED;
+  *block_m = kBlockM;
+  *block_n = kBlockN;
+  return ATTN_JVP_OK;
+}
+
+int attn_jvp_visible_tiles(int N, int dtype, int d, const attn_jvp_mask *mask,
+                           int64_t *tiles_per_block) {
+  int bm, bn;
+  const int st = attn_jvp_tile_shape(dtype, d, &bm, &bn);
+  if (st != ATTN_JVP_OK) return st;
+  if (N <= 0 || !tiles_per_block) return ATTN_JVP_EINVAL;
+  const int mst = check_mask(mask, N);
+  if (mst != ATTN_JVP_OK) return mst;
+  const MaskDev m = to_dev(mask);
+  const int nqb = (N + bm - 1) / bm;
+  for (int qb = 0; qb < nqb; ++qb) {
+    const int q0 = qb * bm;
+    const int q1 = q0 + bm < N ? q0 + bm : N;
+    const TileRanges tr = visible_tiles(m, q0, q1, N, bn);
+    int64_t c = 0;
+    for (int i = 0; i < tr.n; ++i) c += tr.hi[i] - tr.lo[i];
+    tiles_per_block[qb] = c;
+  }
+  return ATTN_JVP_OK;
+}
+
+const char *attn_jvp_status_string(int status) {
+  switch (status) {
+    case ATTN_JVP_OK: return "ok";
+    case ATTN_JVP_EINVAL: return "invalid argument (null pointer, size or dtype)";
+    case ATTN_JVP_EUNSUPPORTED: return "unsupported head dimension for this dtype";
+    case ATTN_JVP_ESTRIDE:
+      return "bad layout (tangent strides differ from the primal's, misaligned "
+             "pointer or stride, or outputs overlapping inputs)";
+    case ATTN_JVP_EMASK: return "inconsistent mask descriptor";
+    case ATTN_JVP_EHIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

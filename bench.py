@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Throughput of the fused attention JVP (O, dO, LSE, dLSE) on one MI355X.
+
+One step is one attn_jvp_fwd call over the whole workload with the inputs
+already resident in HBM.  The timed region is bracketed by device
+synchronisation and timed with HIP events recorded on the stream the kernel
+is launched on.  Counted FLOPs are 12 * (visible query-key pairs) * d per
+(batch, head): the six N^2 d products of the definition (QK^T, dQ K^T,
+Q dK^T, P V, P dV, (P . dS) V).
+
+Prints one JSON line.  ``--gpus`` above 1 is refused: this path runs on one
+GPU.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention-JVP TFLOP/s (fwd+tangent) and % of bf16 MFMA peak, 1 GPU"
+# MI355X dense MFMA peaks, TFLOP/s
+PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}
+NAMES = ("q", "k", "v", "dq", "dk", "dv")
+KERNEL_SOURCE = os.path.join(ROOT, "attention_jvp_amd", "csrc", "attn_jvp.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def visible_pairs(N, mask):
+    """Number of (query, key) pairs the frame-window mask leaves visible."""
+    if mask is None:
+        return N * N
+    F, T, C = mask["frames"], mask["tokens_per_frame"], mask["chunk_frames"]
+    R = mask["radius_chunks"]
+    anchors = set()
+    if mask.get("anchor_first", 1):
+        anchors.add(0)
+    if mask.get("anchor_last", 1):
+        anchors.add(F - 1)
+    total = 0
+    for qf in range(F):
+        if mask.get("anchor_queries_see_all", 0) and qf in anchors:
+            total += F
+            continue
+        seen = {f for f in range(F) if abs(f // C - qf // C) <= R} | anchors
+        total += len(seen)
+    return total * T * T
+
+
+def kernel_sha():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_record(workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sha256") != kernel_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p["num_threads"] for p in threadpool_info() if p.get("user_api") == "blas"]
+        if n:
+            return max(n)
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(w, x, target_s):
+    """Time the float64 oracle on a bounded row sample of the same workload."""
+    import numpy as np
+    from oracle import FrameWindow, attention_jvp_rows
+
+    vis = None
+    if x["mask"] is not None:
+        m = x["mask"]
+        vis = FrameWindow(m["frames"], m["tokens_per_frame"], m["chunk_frames"],
+                          m["radius_chunks"], bool(m["anchor_first"]), bool(m["anchor_last"]),
+                          bool(m["anchor_queries_see_all"]))
+    arrs = [x[n].float().numpy() for n in NAMES]
+
+    def run(nrows):
+        rows = np.linspace(0, w.N - 1, nrows).astype(np.int64)
+        t0 = time.perf_counter()
+        attention_jvp_rows(*arrs, rows, visible=vis)
+        return time.perf_counter() - t0, rows
+
+    dt, _ = run(16)                                    # calibration
+    per_row = dt / 16
+    nrows = int(max(16, min(w.N, target_s / max(per_row, 1e-9))))
+    dt, rows = run(nrows)
+    if vis is None:
+        pairs = len(rows) * w.N
+    else:
+        pairs = int(vis(rows, np.arange(w.N)).sum())
+    flops = 12.0 * w.B * w.H * pairs * w.d
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": blas_threads(),
+        "kind": "oracle",
+        "sample": (f"{len(rows)} evenly spaced query rows x {w.B * w.H} heads of {w.name} "
+                   f"against all {w.N} keys, float64 numpy; {dt:.1f} s"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="image_dit_4096")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target length of the timed oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this attention-JVP path has no "
+              "multi-GPU form here (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import attention_jvp_amd as aj
+    from synth import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    log(f"workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype}")
+    x = make_inputs(w)
+    g = [x[n].cuda() for n in NAMES]
+    o = torch.empty_like(g[0])
+    do = torch.empty_like(o)
+    lse = torch.empty((w.B, w.H, w.N), device="cuda", dtype=torch.float32)
+    dlse = torch.empty_like(lse)
+    outs = (o, do, lse, dlse)
+    mask = x["mask"]
+
+    def step():
+        aj.fwd(*g, mask=mask, out=outs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    pairs = visible_pairs(w.N, mask)
+    flops = 12.0 * w.B * w.H * pairs * w.d
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    log(f"{ms:.4f} ms/step, {tflops:.1f} TFLOP/s ({100 * tflops / peak:.1f}% of {peak} peak)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the float64 oracle on a row sample")
+        cpu = cpu_baseline(w, x, args.cpu_seconds)
+        log(f"oracle: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "pct_of_peak": round(100 * tflops / peak, 2),
+        "config": {
+            "workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+            "mask": mask, "visible_pairs_per_head": pairs,
+            "counted_flops": flops,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / peak, 4),
+            "traffic": traffic_record(w.name),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,148 @@
+/*
+ * attn_jvp.h -- fused attention forward-mode derivative (JVP) on AMD gfx950.
+ *
+ * One online-softmax pass computes, per batch b, head h and query row i,
+ *
+ *   S    = s * Q K^T                       (scores, s = scale)
+ *   dS   = s * (dQ K^T + Q dK^T)           (score tangent)
+ *   P    = softmax_row(S)                  (masked keys get S = -inf, dS = 0)
+ *   O    = P V
+ *   LSE  = log sum_j exp(S_ij)             (natural log)
+ *   dLSE = sum_j P_ij dS_ij                (tangent of LSE)
+ *   dO   = P dV + (P (.) dS) V - dLSE (.) O
+ *
+ * Definitions: page "带分数正则的一致性蒸馏" (gitcode.csdn.net), section
+ * 注意力 -- the attention formula (普通注意力的实现), the chain rule
+ * t_o = P t_v + t_p V with t_p = P (.) t_s - (P t_s^T) P and
+ * t_s = t_q K^T + Q t_k^T, the streaming form with extra state r, A, B, and the
+ * 前向 kernel's op contract (shape rules, tangents sharing the primals'
+ * strides, default scale d^-1/2, outputs allocated by the caller, O and dO in
+ * the input dtype, LSE in float32).  dLSE is the derivative of the stored
+ * log-sum-exp; the pages' kernel computes it (r / l) but does not store it.
+ * The optional frame-window mask follows the page "VDN-Minimax-H3 ... Stage
+ * A1" (yfxerp.com): chunked window of `chunk_frames` frames, `radius_chunks`
+ * chunks on each side, first/last frames as always-visible anchor keys.
+ *
+ * Conventions shared by every entry point:
+ *   - Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE are DEVICE pointers owned by the
+ *     caller; the library allocates and frees no device memory.
+ *   - Tensors are logically [B, H, N, d] (queries and keys have the same N).
+ *     The last (d) dimension must be contiguous; the other strides are
+ *     given in ELEMENTS.  Tangents must use exactly the strides of their
+ *     primal (dQ of Q, dK of K, dV of V, dO of O), as the pages require.
+ *   - Every row start must be 16-byte aligned: base pointers aligned to 16
+ *     bytes and strides multiples of 8 elements (bf16) or 4 (float32).
+ *   - LSE and dLSE are float32, contiguous [B, H, N].
+ *   - O, dO, LSE, dLSE must not alias any input.
+ *   - The call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream).  Arguments are validated on the host before anything is
+ *     launched; on error nothing is launched and a negative status returns.
+ *   - No C++ exception crosses this interface.  The library keeps no state
+ *     between calls and is safe to call from several host threads.
+ *   - Calls that run concurrently on one device race only if their outputs
+ *     overlap.
+ */
+#ifndef ATTN_JVP_H
+#define ATTN_JVP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of Q, K, V, dQ, dK, dV, O and dO.  Accumulation is float32. */
+typedef enum {
+  ATTN_JVP_BF16 = 0, /* bfloat16 in and out; P and P (.) dS rounded to bf16
+                        (round to nearest even) before the value products */
+  ATTN_JVP_FP32 = 1  /* float32 throughout */
+} attn_jvp_dtype;
+
+typedef enum {
+  ATTN_JVP_OK = 0,
+  ATTN_JVP_EINVAL = -1,      /* null pointer, non-positive size, bad dtype  */
+  ATTN_JVP_EUNSUPPORTED = -2,/* head dim not built (built: 64, 128)         */
+  ATTN_JVP_ESTRIDE = -3,     /* tangent strides differ from the primal's, a
+                                misaligned pointer or stride, or overlap    */
+  ATTN_JVP_EMASK = -4,       /* inconsistent mask descriptor                */
+  ATTN_JVP_EHIP = -5         /* the HIP runtime reported an error at launch */
+} attn_jvp_status;
+
+enum { ATTN_JVP_MASK_NONE = 0, ATTN_JVP_MASK_FRAME_WINDOW = 1 };
+
+/* Optional key mask; pass NULL (or kind = ATTN_JVP_MASK_NONE) for dense,
+ * non-causal attention.  For ATTN_JVP_MASK_FRAME_WINDOW the N tokens are
+ * frames * tokens_per_frame tokens flattened frame-major (token i is in frame
+ * i / tokens_per_frame); chunks are runs of chunk_frames frames from frame 0.
+ * Key j is visible to query i iff
+ *     |chunk(frame(i)) - chunk(frame(j))| <= radius_chunks
+ *  or (anchor_first && frame(j) == 0) or (anchor_last && frame(j) == frames-1)
+ *  or (anchor_queries_see_all && frame(i) is an enabled anchor frame).
+ * Requires frames * tokens_per_frame == N, chunk_frames >= 1,
+ * radius_chunks >= 0, otherwise ATTN_JVP_EMASK.  Every query sees its own
+ * frame, so no row is empty.  Tiles of keys that no query of a query block
+ * can see are neither loaded nor computed. */
+typedef struct {
+  int32_t kind;
+  int32_t frames;
+  int32_t tokens_per_frame;
+  int32_t chunk_frames;
+  int32_t radius_chunks;
+  int32_t anchor_first;
+  int32_t anchor_last;
+  int32_t anchor_queries_see_all;
+} attn_jvp_mask;
+
+/* Element strides (batch, head, row) of each tensor; the d stride is 1. */
+typedef struct {
+  int64_t q[3], k[3], v[3];
+  int64_t dq[3], dk[3], dv[3];
+  int64_t o[3], dout[3];
+} attn_jvp_layout;
+
+/* Contiguous [B, H, N, d] tensors.  scale <= 0 selects 1/sqrt(d).
+ * Returns an attn_jvp_status. */
+int attn_jvp_fwd(const void *Q, const void *K, const void *V,
+                 const void *dQ, const void *dK, const void *dV,
+                 void *O, void *dO, float *LSE, float *dLSE,
+                 int B, int H, int N, int d, float scale, int dtype,
+                 const attn_jvp_mask *mask, void *stream);
+
+/* Same computation for strided views (e.g. a [B, N, H, d] buffer seen as
+ * [B, H, N, d]); `layout` gives every tensor's strides and must not be NULL. */
+int attn_jvp_fwd_strided(const void *Q, const void *K, const void *V,
+                         const void *dQ, const void *dK, const void *dV,
+                         void *O, void *dO, float *LSE, float *dLSE,
+                         int B, int H, int N, int d, float scale, int dtype,
+                         const attn_jvp_layout *layout,
+                         const attn_jvp_mask *mask, void *stream);
+
+/* Host-only argument check of attn_jvp_fwd_strided: the status that call
+ * would return before launching (never touches the GPU; device pointers are
+ * only inspected for NULL and alignment). */
+int attn_jvp_check(const void *Q, const void *K, const void *V,
+                   const void *dQ, const void *dK, const void *dV,
+                   void *O, void *dO, float *LSE, float *dLSE,
+                   int B, int H, int N, int d, int dtype,
+                   const attn_jvp_layout *layout, const attn_jvp_mask *mask);
+
+/* Host-only: the query-block rows (block_m) and key-tile length (block_n) the
+ * library uses for (dtype, d); returns a status. */
+int attn_jvp_tile_shape(int dtype, int d, int *block_m, int *block_n);
+
+/* Host-only: the key tiles the scheduler visits for each query block of an
+ * N-token sequence under `mask` (NULL = dense) with the tile shape of
+ * (dtype, d).  Writes ceil(N / block_m) counts into tiles_per_block (host
+ * memory, caller-owned) and returns a status.  This is the exact work list
+ * the kernel walks. */
+int attn_jvp_visible_tiles(int N, int dtype, int d, const attn_jvp_mask *mask,
+                           int64_t *tiles_per_block);
+
+/* Static English text for a status code. */
+const char *attn_jvp_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_JVP_H */

@@ -1,0 +1,174 @@
+"""Host-only checks of the C-ABI library: it loads, exports every function the
+header declares, validates arguments without launching, and its tile
+scheduler visits exactly the key tiles the oracle's mask makes visible.
+No test here touches a GPU."""
+
+import os
+import re
+
+import numpy as np
+import pytest
+
+import attention_jvp_amd as aj
+from oracle import FrameWindow
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_jvp.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_jvp_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    declared = _declared_functions()
+    assert "attn_jvp_fwd" in declared and "attn_jvp_fwd_strided" in declared
+    lib = aj.load()
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(aj.exported_symbols()) == declared
+
+
+def _layout(B, H, N, d):
+    s = (H * N * d, N * d, d)
+    lay = aj.Layout()
+    for n in ("q", "k", "v", "dq", "dk", "dv", "o", "dout"):
+        getattr(lay, n)[:] = s
+    return lay
+
+
+def _ptrs(B, H, N, d, esize, gap=1 << 20):
+    """Fake, well-separated, 256-byte aligned device addresses (never used)."""
+    size = B * H * N * d * esize + gap
+    base = 1 << 40
+    return [base + i * size for i in range(10)]
+
+
+def _check(B=1, H=2, N=100, d=128, dtype=0, lay=None, mask=None, ptrs=None):
+    esize = 2 if dtype == 0 else 4
+    p = _ptrs(B, H, N, d, esize) if ptrs is None else ptrs
+    lay = _layout(B, H, N, d) if lay is None else lay
+    return aj.attn_jvp_check(*p, B, H, N, d, dtype, lay, mask)
+
+
+def test_valid_arguments():
+    assert _check() == 0
+    assert _check(d=64) == 0
+    assert _check(d=64, dtype=1) == 0
+    assert _check(N=65520, H=1, mask=dict(frames=42, tokens_per_frame=1560, chunk_frames=5,
+                                          radius_chunks=1)) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), -1), (dict(H=-1), -1), (dict(N=0), -1), (dict(dtype=7), -1),
+    (dict(d=96), -2), (dict(d=256), -2), (dict(d=128, dtype=1), -2),
+])
+def test_rejected_sizes(kw, status):
+    assert _check(**kw) == status
+
+
+def test_null_pointers_and_layout():
+    p = _ptrs(1, 2, 100, 128, 2)
+    for i in range(10):
+        q = list(p)
+        q[i] = None
+        assert aj.attn_jvp_check(*q, 1, 2, 100, 128, 0, _layout(1, 2, 100, 128), None) == -1
+    assert aj.attn_jvp_check(*p, 1, 2, 100, 128, 0, None, None) == -1
+
+
+def test_tangent_strides_must_match_primal():
+    for name in ("dq", "dk", "dv", "dout"):
+        lay = _layout(1, 2, 100, 128)
+        getattr(lay, name)[0] += 8
+        assert _check(lay=lay) == -3, name
+
+
+def test_alignment_and_overlap():
+    lay = _layout(1, 2, 100, 128)
+    lay.k[2] = 132            # row stride not a multiple of 8 bf16
+    lay.dk[2] = 132
+    assert _check(lay=lay) == -3
+    p = _ptrs(1, 2, 100, 128, 2)
+    p[1] += 2                  # K not 16-byte aligned
+    assert _check(ptrs=p) == -3
+    p = _ptrs(1, 2, 100, 128, 2)
+    p[6] = p[0] + 256          # O overlaps Q
+    assert _check(ptrs=p) == -3
+    p = _ptrs(1, 2, 100, 128, 2)
+    p[9] = p[8] + 4            # dLSE overlaps LSE
+    assert _check(ptrs=p) == -3
+    # a [B, N, H, d] buffer viewed as [B, H, N, d] is a valid layout
+    B, H, N, d = 2, 3, 50, 64
+    lay = aj.Layout()
+    for n in ("q", "k", "v", "dq", "dk", "dv", "o", "dout"):
+        getattr(lay, n)[:] = (N * H * d, d, H * d)
+    assert _check(B=B, H=H, N=N, d=d, lay=lay) == 0
+
+
+@pytest.mark.parametrize("mask", [
+    dict(frames=41, tokens_per_frame=1560, chunk_frames=5, radius_chunks=1),
+    dict(frames=42, tokens_per_frame=1560, chunk_frames=0, radius_chunks=1),
+    dict(frames=42, tokens_per_frame=1560, chunk_frames=5, radius_chunks=-1),
+])
+def test_bad_mask(mask):
+    assert _check(N=65520, H=1, mask=mask) == -4
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -5):
+        assert aj.attn_jvp_status_string(s)
+    assert aj.attn_jvp_status_string(-99) == "unknown status"
+
+
+def test_tile_shape():
+    assert aj.attn_jvp_tile_shape(0, 128) == (128, 64)
+    assert aj.attn_jvp_tile_shape(1, 64) == (128, 64)
+    with pytest.raises(aj.AttnJvpError):
+        aj.attn_jvp_tile_shape(1, 128)
+
+
+def _tiles_with_visible_pairs(w, N, bm, bn):
+    """Brute force with the oracle's mask: key tiles holding at least one
+    visible (query, key) pair, per query block."""
+    out = []
+    kidx = np.arange(N)
+    for q0 in range(0, N, bm):
+        rows = np.arange(q0, min(q0 + bm, N))
+        # visibility depends on the query's frame only: one row per frame
+        _, first = np.unique(rows // w.tokens_per_frame, return_index=True)
+        vis = w(rows[first], kidx).any(axis=0)
+        tiles = {j // bn for j in np.nonzero(vis)[0]}
+        out.append(len(tiles))
+    return out
+
+
+@pytest.mark.parametrize("F,T,C,R,first,last,see_all", [
+    (42, 1560, 5, 1, 1, 1, 0),
+    (42, 1560, 5, 1, 1, 1, 1),
+    (21, 100, 3, 1, 1, 0, 0),
+    (17, 37, 2, 0, 0, 1, 0),
+    (9, 300, 4, 2, 0, 0, 0),
+    (50, 7, 1, 0, 1, 1, 1),
+])
+def test_scheduler_visits_exactly_the_visible_tiles(F, T, C, R, first, last, see_all):
+    N = F * T
+    mask = dict(frames=F, tokens_per_frame=T, chunk_frames=C, radius_chunks=R,
+                anchor_first=first, anchor_last=last, anchor_queries_see_all=see_all)
+    got = aj.attn_jvp_visible_tiles(N, 0, 128, mask)
+    w = FrameWindow(F, T, C, R, bool(first), bool(last), bool(see_all))
+    bm, bn = aj.attn_jvp_tile_shape(0, 128)
+    assert got == _tiles_with_visible_pairs(w, N, bm, bn)
+
+
+def test_dense_scheduler_visits_every_tile():
+    got = aj.attn_jvp_visible_tiles(4352, 0, 64)
+    assert got == [68] * 34
+
+
+def test_long_video_visited_fraction():
+    mask = dict(frames=42, tokens_per_frame=1560, chunk_frames=5, radius_chunks=1)
+    got = aj.attn_jvp_visible_tiles(65520, 0, 128, mask)
+    total = len(got) * ((65520 + 63) // 64)
+    assert 0.36 < sum(got) / total < 0.38

@@ -1,0 +1,242 @@
+"""GPU parity: the HIP path (through the C-ABI) against the float64 oracle.
+
+Tolerances (stated for the path): float32 inputs, normwise
+max|gpu - ref| / max|ref| <= 1e-5 for O (and LSE) and <= 1e-4 for dO (and
+dLSE); bf16 inputs, the same normwise error <= 2e-2 for every output.  Small
+shapes are compared element by element on every row; the full-size workloads
+on a deterministic row sample, in the launch configuration the benchmark
+times.
+"""
+
+import ctypes
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import attention_jvp_amd as aj
+from oracle import FrameWindow, attention_jvp, attention_jvp_rows
+from synth import WORKLOADS, Workload, make_inputs, sample_rows, to_float64
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": (1e-5, 1e-4), "bf16": (2e-2, 2e-2)}
+NAMES = ("q", "k", "v", "dq", "dk", "dv")
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _dev(x):
+    return {n: x[n].cuda() for n in NAMES}
+
+
+def _run(x, mask=None, scale=None):
+    g = _dev(x)
+    out = aj.fwd(*(g[n] for n in NAMES), scale=scale, mask=mask)
+    torch.cuda.synchronize()
+    return out
+
+
+def _err(got, ref):
+    den = np.max(np.abs(ref[np.isfinite(ref)])) if np.isfinite(ref).any() else 1.0
+    return float(np.max(np.abs(got - ref)) / max(den, 1e-30))
+
+
+def _compare(gpu, ref, dtype, what):
+    tol_o, tol_do = TOL[dtype]
+    names = ("O", "dO", "LSE", "dLSE")
+    tols = (tol_o, tol_do, tol_o, tol_do)
+    errs = {}
+    for n, g, r, t in zip(names, gpu, ref, tols):
+        assert np.array_equal(np.isfinite(g), np.isfinite(r)), f"{what}: {n} finiteness"
+        fin = np.isfinite(r)
+        if n == "LSE":
+            assert np.array_equal(g[~fin], r[~fin]), f"{what}: LSE -inf rows"
+        e = _err(g[fin], r[fin]) if fin.any() else 0.0
+        errs[n] = e
+        assert e <= t, f"{what}: {n} normwise error {e:.3e} > {t:.0e}"
+    _say(what, " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    return errs
+
+
+def _full_check(w, mask=None, scale=None, seed=None):
+    x = make_inputs(w, seed=seed)
+    mask = x["mask"] if mask is None else mask
+    out = _run(x, mask=mask, scale=scale)
+    gpu = [to_float64(t) for t in out]
+    vis = None if mask is None else FrameWindow(**{k: bool(v) if k.startswith("anchor") else v
+                                                   for k, v in mask.items()})
+    ref = attention_jvp(*(to_float64(x[n]) for n in NAMES), scale=scale, visible=vis)
+    return _compare(gpu, ref, w.dtype, f"{w.name} B{w.B} H{w.H} N{w.N} d{w.d}")
+
+
+# ---- small shapes: every row, several tiles, ragged tails -----------------
+
+SMALL = [
+    ("fp32", 1, 2, 128, 64), ("fp32", 1, 1, 1, 64), ("fp32", 2, 1, 77, 64),
+    ("fp32", 1, 1, 300, 64),
+    ("bf16", 1, 2, 256, 128), ("bf16", 1, 1, 1, 128), ("bf16", 1, 1, 63, 128),
+    ("bf16", 1, 1, 65, 128), ("bf16", 2, 2, 129, 128), ("bf16", 1, 2, 333, 128),
+    ("bf16", 1, 1, 1, 64), ("bf16", 2, 2, 200, 64), ("bf16", 1, 3, 517, 64),
+]
+
+
+@pytest.mark.parametrize("dtype,B,H,N,d", SMALL)
+def test_small_shapes_every_row(dtype, B, H, N, d):
+    _say(f"small {dtype} B{B} H{H} N{N} d{d}")
+    w = Workload("small", B, H, N, d, dtype, 77 + N + d, tangent_scale=0.1)
+    _full_check(w)
+
+
+def test_tiny_fp32_workload():
+    _full_check(WORKLOADS["tiny_fp32"])
+
+
+def test_custom_scale():
+    w = Workload("scale", 1, 2, 190, 128, "bf16", 5, tangent_scale=0.3)
+    _full_check(w, scale=0.05)
+
+
+def test_small_trigflow_and_rms_recipe():
+    w = Workload("trig", 1, 2, 300, 128, "bf16", 6, rms_qk=True, tangents="trigflow")
+    _full_check(w)
+
+
+def test_large_logits_bf16():
+    # scores of magnitude ~ 30: the running max and rescaling matter
+    w = Workload("big", 1, 2, 400, 64, "bf16", 8, tangent_scale=0.1)
+    _full_check(w, scale=4.0)
+
+
+@pytest.mark.parametrize("F,T,C,R,first,last,see_all,dtype,d", [
+    (7, 37, 2, 1, 1, 1, 0, "bf16", 128),
+    (9, 64, 3, 0, 1, 0, 0, "bf16", 64),
+    (6, 50, 2, 0, 0, 1, 1, "bf16", 128),
+    (11, 40, 1, 1, 1, 1, 0, "fp32", 64),
+    (5, 100, 5, 0, 0, 0, 0, "bf16", 128),
+])
+def test_frame_window_mask_every_row(F, T, C, R, first, last, see_all, dtype, d):
+    N = F * T
+    _say(f"mask F{F} T{T} C{C} R{R} a{first}{last}{see_all} {dtype} d{d}")
+    mask = dict(frames=F, tokens_per_frame=T, chunk_frames=C, radius_chunks=R,
+                anchor_first=first, anchor_last=last, anchor_queries_see_all=see_all)
+    w = Workload("mask", 1, 2, N, d, dtype, 900 + N, tangent_scale=0.1)
+    _full_check(w, mask=mask)
+
+
+def test_strided_bshd_views():
+    # tensors stored [B, N, H, d] and passed as [B, H, N, d] views
+    B, H, N, d = 2, 3, 150, 128
+    w = Workload("bshd", B, H, N, d, "bf16", 11, tangent_scale=0.1)
+    x = make_inputs(w)
+    g = {n: x[n].transpose(1, 2).contiguous().cuda().transpose(1, 2) for n in NAMES}
+    assert g["q"].stride() == (N * H * d, d, H * d, 1)
+    out = aj.fwd(*(g[n] for n in NAMES))
+    torch.cuda.synchronize()
+    ref = attention_jvp(*(to_float64(x[n]) for n in NAMES))
+    _compare([to_float64(t) for t in out], ref, "bf16", "bshd")
+
+
+def test_contiguous_entry_point_raw_pointers():
+    w = Workload("raw", 1, 2, 200, 64, "bf16", 12, tangent_scale=0.1)
+    x = make_inputs(w)
+    g = _dev(x)
+    o = torch.empty_like(g["q"])
+    do = torch.empty_like(o)
+    lse = torch.empty((1, 2, 200), device="cuda", dtype=torch.float32)
+    dlse = torch.empty_like(lse)
+    st = aj.attn_jvp_fwd(*(g[n].data_ptr() for n in NAMES), o.data_ptr(), do.data_ptr(),
+                         lse.data_ptr(), dlse.data_ptr(), 1, 2, 200, 64, 0.0,
+                         aj.ATTN_JVP_BF16, None, torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    ref = attention_jvp(*(to_float64(x[n]) for n in NAMES))
+    _compare([to_float64(t) for t in (o, do, lse, dlse)], ref, "bf16", "raw")
+
+
+def test_errors_launch_nothing():
+    w = Workload("err", 1, 1, 64, 128, "bf16", 13)
+    g = _dev(make_inputs(w))
+    with pytest.raises(aj.AttnJvpError) as e:
+        aj.fwd(g["q"], g["k"], g["v"], g["dq"].transpose(2, 3).contiguous().transpose(2, 3),
+               g["dk"], g["dv"])
+    assert e.value.status == -3
+    bad = {n: g[n][..., :96].contiguous() for n in NAMES}
+    with pytest.raises(aj.AttnJvpError) as e:
+        aj.fwd(*(bad[n] for n in NAMES))
+    assert e.value.status == -2
+
+
+def test_bitwise_deterministic():
+    w = Workload("det", 2, 4, 1000, 128, "bf16", 14, tangent_scale=0.1)
+    g = _dev(make_inputs(w))
+    a = aj.fwd(*(g[n] for n in NAMES))
+    b = aj.fwd(*(g[n] for n in NAMES))
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_nan_in_one_query_row_stays_in_that_row():
+    w = Workload("nan", 1, 2, 300, 128, "bf16", 15, tangent_scale=0.1)
+    x = make_inputs(w)
+    x["q"][0, 1, 137, 5] = float("nan")
+    o, do, lse, dlse = _run(x)
+    bad = torch.isnan(o).any(-1) | torch.isnan(do).any(-1) | torch.isnan(lse) | torch.isnan(dlse)
+    expect = torch.zeros_like(bad)
+    expect[0, 1, 137] = True
+    assert torch.equal(bad.cpu(), expect.cpu())
+
+
+def test_zero_score_tangent_matches_output_with_dv_bitwise():
+    # dQ = dK = 0: the tangent accumulator sums exactly the products the
+    # output accumulator sums when V is replaced by dV
+    w = WORKLOADS["image_dit_4096"]
+    small = Workload("zst", 1, 4, w.N, w.d, "bf16", 16)
+    x = make_inputs(small)
+    g = _dev(x)
+    z = torch.zeros_like(g["q"])
+    o, do, lse, dlse = aj.fwd(g["q"], g["k"], g["v"], z, z, g["dv"])
+    o2, _, _, _ = aj.fwd(g["q"], g["k"], g["dv"], z, z, g["dv"])
+    torch.cuda.synchronize()
+    assert torch.equal(do, o2)
+    assert torch.all(dlse == 0)
+
+
+# ---- full-size workloads, sampled rows --------------------------------------
+
+def _sampled_check(name, every):
+    w = WORKLOADS[name]
+    _say(f"workload {name}: generating inputs")
+    x = make_inputs(w)
+    _say(f"workload {name}: running GPU")
+    out = _run(x, mask=x["mask"])
+    m = x["mask"]
+    rows = sample_rows(w.N, every=every, tokens_per_frame=m["tokens_per_frame"] if m else None)
+    idx = torch.from_numpy(rows).cuda()
+    gpu = [to_float64(t.index_select(2, idx)) for t in out]
+    vis = None if m is None else FrameWindow(**{k: bool(v) if k.startswith("anchor") else v
+                                                for k, v in m.items()})
+    _say(f"workload {name}: oracle on {len(rows)} rows x {w.B * w.H} heads")
+    # float32 holds every bf16 value exactly; the oracle widens to float64
+    ref = attention_jvp_rows(*(x[n].float().numpy() for n in NAMES), rows, visible=vis)
+    return _compare(gpu, ref, w.dtype, f"{name} ({len(rows)} rows/head)")
+
+
+def test_workload_image_dit_4096():
+    _sampled_check("image_dit_4096", every=32)
+
+
+def test_workload_t2i_prefix_4352():
+    _sampled_check("t2i_prefix_4352", every=32)
+
+
+def test_workload_video_dit_32760():
+    _sampled_check("video_dit_32760", every=256)
+
+
+def test_workload_long_video_65520():
+    _sampled_check("long_video_65520", every=512)
