@@ -160,10 +160,16 @@ def test_contiguous_entry_point_raw_pointers():
 def test_errors_launch_nothing():
     w = Workload("err", 1, 1, 64, 128, "bf16", 13)
     g = _dev(make_inputs(w))
+    # a tangent whose row stride differs from its primal's: rejected by the C side
+    wide = torch.zeros((1, 1, 64, 136), device="cuda", dtype=torch.bfloat16)
+    wide[..., :128] = g["dq"]
     with pytest.raises(aj.AttnJvpError) as e:
+        aj.fwd(g["q"], g["k"], g["v"], wide[..., :128], g["dk"], g["dv"])
+    assert e.value.status == -3
+    # a non-contiguous head dimension cannot be described to the C side
+    with pytest.raises(ValueError):
         aj.fwd(g["q"], g["k"], g["v"], g["dq"].transpose(2, 3).contiguous().transpose(2, 3),
                g["dk"], g["dv"])
-    assert e.value.status == -3
     bad = {n: g[n][..., :96].contiguous() for n in NAMES}
     with pytest.raises(aj.AttnJvpError) as e:
         aj.fwd(*(bad[n] for n in NAMES))
