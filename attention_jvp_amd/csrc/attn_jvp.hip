@@ -15,12 +15,17 @@
 //     cross-lane step, the row sums stay lane-local until the epilogue, and
 //     the score fragment is already the B operand of the value products;
 //   * Q and dQ stay in registers (B operands) for the whole key loop;
-//   * K, dK are staged row-major in LDS (A operands of S^T and dS^T);
-//     V, dV are staged TRANSPOSED in LDS, with 4-key groups permuted inside
-//     each 16-key run so that a lane's 8 operand values are one 16-byte read;
+//   * K, dK, V, dV tiles move global -> LDS with asynchronous
+//     global_load_lds_dwordx4 copies into two LDS stages (the next tile
+//     streams in while the current one is consumed; no register staging),
+//     row-major with an XOR swizzle of the 16-byte chunks;
+//   * the value products need V and dV transposed (keys along the MFMA k
+//     dimension): ds_read_b64_tr_b16 transposes 4 keys x 4 columns per
+//     16-lane group on the way out of LDS;
 //   * O^T and T^T (= (A~ + B~)^T) accumulate in 32x32 fp32 fragments: every
 //     value a lane holds belongs to its own query, so the online rescale is
-//     one multiply by a per-lane factor;
+//     one multiply by a per-lane factor, and it is skipped unless the row
+//     max grew by more than 2^8;
 //   * exp2 domain for the scores (scale * log2 e folded into one FMA), the
 //     tangent stays in natural units;
 //   * workgroup ids are remapped so that all query blocks of one (b, h) land
@@ -120,25 +125,26 @@ __host__ __device__ inline TileRanges visible_tiles(const MaskDev &m, int q_lo,
   if (f_lo < 0) f_lo = 0;
   long long f_hi_l = (long long)(c1 + R + 1) * C;
   int f_hi = f_hi_l > F ? F : (int)f_hi_l;
-  // key intervals, then tiles
-  int klo[3], khi[3], n = 0;
-  if (m.first) { klo[n] = 0; khi[n] = T; ++n; }
-  klo[n] = f_lo * T; khi[n] = f_hi * T; ++n;
-  if (m.last) { klo[n] = (F - 1) * T; khi[n] = F * T; ++n; }
-  int tlo[3], thi[3];
-  for (int i = 0; i < n; ++i) {
-    tlo[i] = klo[i] / BN;
-    thi[i] = (khi[i] + BN - 1) / BN;
-  }
-  // intervals are already ascending by start; merge overlaps and contacts
+  // candidate key-tile intervals in ascending order of start: first-frame
+  // anchor, chunk window, last-frame anchor; merged where they touch
+  // (static indices only, so nothing is spilled to memory)
   tr.n = 0;
-  for (int i = 0; i < n; ++i) {
-    if (tr.n > 0 && tlo[i] <= tr.hi[tr.n - 1]) {
-      if (thi[i] > tr.hi[tr.n - 1]) tr.hi[tr.n - 1] = thi[i];
+  tr.lo[0] = tr.hi[0] = tr.lo[1] = tr.hi[1] = tr.lo[2] = tr.hi[2] = 0;
+  const bool valid[3] = {m.first != 0, true, m.last != 0};
+  const int a_[3] = {0, f_lo * T / BN, (F - 1) * T / BN};
+  const int z_[3] = {(T + BN - 1) / BN, (f_hi * T + BN - 1) / BN, (F * T + BN - 1) / BN};
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    if (!valid[i]) continue;
+    const int a = a_[i], z = z_[i];
+    if (tr.n == 0) {
+      tr.lo[0] = a; tr.hi[0] = z; tr.n = 1;
+    } else if (tr.n == 1) {
+      if (a <= tr.hi[0]) tr.hi[0] = z > tr.hi[0] ? z : tr.hi[0];
+      else { tr.lo[1] = a; tr.hi[1] = z; tr.n = 2; }
     } else {
-      tr.lo[tr.n] = tlo[i];
-      tr.hi[tr.n] = thi[i];
-      ++tr.n;
+      if (a <= tr.hi[1]) tr.hi[1] = z > tr.hi[1] ? z : tr.hi[1];
+      else { tr.lo[2] = a; tr.hi[2] = z; tr.n = 3; }
     }
   }
   return tr;
@@ -167,37 +173,107 @@ __device__ inline int logical_block_id() {
   return x * per + (x < rem ? x : rem) + local;
 }
 
-// Physical column of key `key` (0..BN-1) in a transposed V/dV row: 4-key
-// groups are permuted inside every 16-key run (group bits swapped) so that the
-// 8 keys one lane contributes to a k-step are contiguous.
-__device__ inline int vt_col(int key) {
-  const int g = key >> 2;
-  const int pg = (g & ~3) | ((g & 1) << 1) | ((g >> 1) & 1);
-  return (pg << 2) | (key & 3);
+// ---------------------------------------------------------------------------
+// LDS tile layout.  A K, dK, V or dV tile is BN rows of RB = d * sizeof(T)
+// bytes, row-major (one key per row).  The 16-byte chunks of row r are XOR
+// permuted with swz(r) so that (a) 16 consecutive rows read at one logical
+// chunk (the K operand) and (b) 4 consecutive rows read as a 64-byte run (the
+// transpose reads of V) both touch every bank once.
+// ---------------------------------------------------------------------------
+template <int RB>
+__device__ inline int swz(int r) {
+  constexpr int CPR = RB / 16;            // chunks per row
+  constexpr int RPB = 256 / RB;           // rows per 256-byte bank sweep
+  constexpr int Q = CPR / 4;
+  const int m = r / RPB;
+  return ((m % Q) << 2) | ((m / Q) % 4);
 }
 
-template <typename T, int D, int BN, bool MASKED>
+template <int RB>
+__device__ inline int lds_off(int r, int byte_col) {
+  return r * RB + ((((byte_col >> 4) ^ swz<RB>(r))) << 4) + (byte_col & 15);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Read 4 consecutive-key bf16 values of one d column: ds_read_b64_tr_b16.
+// In each 16-lane group, lane i receives element (i % 4) of the 8-byte chunks
+// addressed by lanes i/4, i/4 + 4, i/4 + 8 and i/4 + 12 (in that order).
+__device__ inline i16x4 lds_read_tr(const char *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
+}
+
+// Issue the asynchronous global->LDS copies of one key tile (K, dK, V, dV)
+// into `stage`.  Each wave instruction fills 1 KiB of LDS contiguously, lane l
+// writing bytes [16 l, 16 l + 16); the lane picks the global chunk that the
+// swizzled layout puts there.  Rows past the end of the sequence re-read row
+// N-1 (their scores are masked to -inf and their tangents to 0).
+template <typename T, int D, int BN>
+__device__ inline void issue_tile(const T *const src[4], const int64_t stride[4],
+                                  int k0, int N, char *stage, int wave, int lane) {
+  constexpr int RB = D * (int)sizeof(T);
+  constexpr int CPR = RB / 16;
+  constexpr int EV = 16 / (int)sizeof(T);
+  constexpr int TILE = BN * RB;
+  constexpr int IPW = TILE / 1024 / kWaves;   // wave instructions per tensor
+  static_assert(IPW * 1024 * kWaves == TILE, "tile must split over the waves");
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int gi = wave * IPW + i;
+    const int s = gi * 64 + lane;
+    const int r = s / CPR;
+    const int c = (s % CPR) ^ swz<RB>(r);
+    int key = k0 + r;
+    key = key < N ? key : N - 1;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const T *g = src[t] + (int64_t)key * stride[t] + c * EV;
+      __builtin_amdgcn_global_load_lds((const void *)g,
+                                       (lds_void *)(stage + t * TILE + gi * 1024), 16, 0, 0);
+    }
+  }
+}
+
+__device__ inline void wait_vmem() {
+  // s_waitcnt vmcnt(0): every global->LDS copy this wave issued has landed
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// Tile index of the idx-th visited tile.
+__device__ inline int tile_at(const TileRanges &tr, int idx) {
+  int t = tr.lo[0] + idx;
+  if (tr.n > 1 && t >= tr.hi[0]) {
+    t = tr.lo[1] + (t - tr.hi[0]);
+    if (tr.n > 2 && t >= tr.hi[1]) t = tr.lo[2] + (t - tr.hi[1]);
+  }
+  return t;
+}
+
+// Lazy rescale: the running max only moves when a tile's max exceeds it by
+// more than 2^8 (P~ then stays below 256); the final normalisation uses the
+// same reference, so the result is unchanged.
+constexpr float kRescaleThreshold = 8.0f;
+
+template <typename T, int D, int BN, int CK, bool MASKED>
 __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
   using E = Elem<T>;
   using Frag = typename E::Frag;
+  constexpr bool BF16 = sizeof(T) == 2;
   constexpr int KL = E::KL;
   constexpr int KI = E::KI;
-  constexpr int EV = 16 / sizeof(T);          // elements per 16-byte vector
-  constexpr int PAD = EV;                     // one 16-byte pad per LDS row
-  constexpr int LDK = D + PAD;                // K/dK LDS row length
-  constexpr int LDV = BN + PAD;               // V^T/dV^T LDS row length
+  constexpr int RB = D * (int)sizeof(T);      // bytes per LDS row
+  constexpr int TILE = BN * RB;               // bytes per tensor tile
+  constexpr int STAGE = 4 * TILE;             // K, dK, V, dV
   constexpr int DS = D / KI;                  // k-steps over d
-  constexpr int NSB = BN / 32;                // 32-key sub-blocks per tile
+  constexpr int NSB = CK / 32;                // 32-key sub-blocks per softmax step
   constexpr int ND = D / 32;                  // 32-wide d blocks
   constexpr int PS = 32 / KI;                 // k-steps per sub-block (P V)
-  constexpr int CPR = D / EV;                 // 16-byte chunks per row
-  static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
+  static_assert(CK % 32 == 0 && BN % CK == 0 && D % 32 == 0, "tile shape");
 
-  __shared__ __attribute__((aligned(16))) T smem[2 * BN * LDK + 2 * D * LDV];
-  T *Ks = smem;
-  T *dKs = Ks + BN * LDK;
-  T *Vt = dKs + BN * LDK;
-  T *dVt = Vt + D * LDV;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -214,12 +290,29 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
 
   const T *Q = (const T *)p.q + b * p.sq[0] + h * p.sq[1];
   const T *dQ = (const T *)p.dq + b * p.sq[0] + h * p.sq[1];
-  const T *K = (const T *)p.k + b * p.sk[0] + h * p.sk[1];
-  const T *dK = (const T *)p.dk + b * p.sk[0] + h * p.sk[1];
-  const T *V = (const T *)p.v + b * p.sv[0] + h * p.sv[1];
-  const T *dV = (const T *)p.dv + b * p.sv[0] + h * p.sv[1];
+  const T *src[4] = {(const T *)p.k + b * p.sk[0] + h * p.sk[1],
+                     (const T *)p.dk + b * p.sk[0] + h * p.sk[1],
+                     (const T *)p.v + b * p.sv[0] + h * p.sv[1],
+                     (const T *)p.dv + b * p.sv[0] + h * p.sv[1]};
+  const int64_t stride[4] = {p.sk[2], p.sk[2], p.sv[2], p.sv[2]};
 
   const int q0 = qb * kBlockM;
+  const int q_hi = (q0 + kBlockM < N) ? q0 + kBlockM : N;
+
+  TileRanges tr;
+  if constexpr (MASKED) {
+    tr = visible_tiles(p.mask, q0, q_hi, N, BN);
+  } else {
+    tr.n = 1;
+    tr.lo[0] = 0;
+    tr.hi[0] = (N + BN - 1) / BN;
+  }
+  int ntile = 0;
+  for (int i = 0; i < tr.n; ++i) ntile += tr.hi[i] - tr.lo[i];
+
+  // first tile in flight before anything else
+  issue_tile<T, D, BN>(src, stride, tile_at(tr, 0) * BN, N, smem, wave, lane);
+
   const int qrow = q0 + wave * kWaveRows + qi;
   const bool qvalid = qrow < N;
 
@@ -243,38 +336,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
     oacc[e] = f32x16{};
     tacc[e] = f32x16{};
   }
-  float m_run = -INFINITY;   // running max, log2 units
-  float l_run = 0.f;         // lane-partial running sum of P~
-  float r_run = 0.f;         // lane-partial running sum of H~
+  float m_run = -INFINITY;   // reference max, log2 units
+  float l_run = 0.f;         // lane-partial sum of P~
+  float r_run = 0.f;         // lane-partial sum of H~
 
   const float scale = p.scale;
   const float c2 = p.scale_log2;
 
-  // query-side mask terms
+  // query-side mask terms; keys in [win_lo, win_hi) and the anchor frames are
+  // visible to every row of this block, so tiles inside them need no mask
   int q_chunk = 0;
   bool q_all = false;
+  int win_lo = 0, win_hi = 0;
   if constexpr (MASKED) {
     const int qf_ = div_fix(qvalid ? qrow : 0, p.mask.tpf, p.mask.inv_tpf);
     q_chunk = div_fix(qf_, p.mask.chunk, p.mask.inv_chunk);
     q_all = p.mask.see_all &&
             ((p.mask.first && qf_ == 0) || (p.mask.last && qf_ == p.mask.frames - 1));
-  }
-
-  TileRanges tr;
-  if constexpr (MASKED) {
-    const int q_hi = (q0 + kBlockM < N) ? q0 + kBlockM : N;
-    tr = visible_tiles(p.mask, q0, q_hi, N, BN);
-  } else {
-    tr.n = 1;
-    tr.lo[0] = 0;
-    tr.hi[0] = (N + BN - 1) / BN;
-  }
-
-  // keys in [win_lo, win_hi) and the anchor frames are visible to every row
-  // of this query block; a tile inside one of them needs no element mask
-  int win_lo = 0, win_hi = 0;
-  if constexpr (MASKED) {
-    const int q_hi = (q0 + kBlockM < N) ? q0 + kBlockM : N;
     const int c0 = (q0 / p.mask.tpf) / p.mask.chunk;
     const int c1 = ((q_hi - 1) / p.mask.tpf) / p.mask.chunk;
     int flo = (c1 - p.mask.radius) * p.mask.chunk;
@@ -287,95 +365,34 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
     }
   }
 
-  for (int ri = 0; ri < tr.n; ++ri) {
-    for (int t = tr.lo[ri]; t < tr.hi[ri]; ++t) {
-      const int k0 = t * BN;
+  for (int it = 0; it < ntile; ++it) {
+    const int k0 = tile_at(tr, it) * BN;
+    const char *st = smem + (it & 1) * STAGE;
+    wait_vmem();
+    __syncthreads();   // tile `it` landed; every wave is done with tile it-1
+    if (it + 1 < ntile)
+      issue_tile<T, D, BN>(src, stride, tile_at(tr, it + 1) * BN, N,
+                           smem + ((it + 1) & 1) * STAGE, wave, lane);
+    const char *Ks = st;
+    const char *dKs = st + TILE;
+    const char *Vs = st + 2 * TILE;
+    const char *dVs = st + 3 * TILE;
 
-      // ---- stage K, dK (row-major) and V, dV (transposed) into LDS ----
-      __syncthreads();   // previous tile fully consumed
-      constexpr int KCH = BN * CPR;            // 16-byte chunks per K tile
 #pragma unroll
-      for (int it = 0; it < (KCH + kThreads - 1) / kThreads; ++it) {
-        const int c = tid + it * kThreads;
-        if (KCH % kThreads != 0 && c >= KCH) break;
-        const int key = c / CPR;
-        const int col = (c - key * CPR) * EV;
-        uint4 kv = {0u, 0u, 0u, 0u}, dkv = {0u, 0u, 0u, 0u};
-        if (k0 + key < N) {
-          const int64_t off = (int64_t)(k0 + key) * p.sk[2] + col;
-          kv = *(const uint4 *)(K + off);
-          dkv = *(const uint4 *)(dK + off);
-        }
-        *(uint4 *)(Ks + key * LDK + col) = kv;
-        *(uint4 *)(dKs + key * LDK + col) = dkv;
-      }
-      constexpr int VCH = (BN / 4) * CPR;      // 4-key x 16-byte blocks
-#pragma unroll
-      for (int it = 0; it < (VCH + kThreads - 1) / kThreads; ++it) {
-        const int c = tid + it * kThreads;
-        if (VCH % kThreads != 0 && c >= VCH) break;
-        const int kg = c / CPR;
-        const int col = (c - kg * CPR) * EV;
-        uint4 vr[4], dvr[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int key = k0 + kg * 4 + j;
-          if (key < N) {
-            const int64_t off = (int64_t)key * p.sv[2] + col;
-            vr[j] = *(const uint4 *)(V + off);
-            dvr[j] = *(const uint4 *)(dV + off);
-          } else {
-            vr[j] = uint4{0u, 0u, 0u, 0u};
-            dvr[j] = uint4{0u, 0u, 0u, 0u};
-          }
-        }
-        const int pc = vt_col(kg * 4);
-        if constexpr (sizeof(T) == 2) {
-          const uint16_t *v16[4], *dv16[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            v16[j] = (const uint16_t *)&vr[j];
-            dv16[j] = (const uint16_t *)&dvr[j];
-          }
-#pragma unroll
-          for (int e = 0; e < EV; ++e) {
-            uint2 w, dw;
-            w.x = (uint32_t)v16[0][e] | ((uint32_t)v16[1][e] << 16);
-            w.y = (uint32_t)v16[2][e] | ((uint32_t)v16[3][e] << 16);
-            dw.x = (uint32_t)dv16[0][e] | ((uint32_t)dv16[1][e] << 16);
-            dw.y = (uint32_t)dv16[2][e] | ((uint32_t)dv16[3][e] << 16);
-            *(uint2 *)(Vt + (col + e) * LDV + pc) = w;
-            *(uint2 *)(dVt + (col + e) * LDV + pc) = dw;
-          }
-        } else {
-          const uint32_t *v32[4], *dv32[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            v32[j] = (const uint32_t *)&vr[j];
-            dv32[j] = (const uint32_t *)&dvr[j];
-          }
-#pragma unroll
-          for (int e = 0; e < EV; ++e) {
-            uint4 w = {v32[0][e], v32[1][e], v32[2][e], v32[3][e]};
-            uint4 dw = {dv32[0][e], dv32[1][e], dv32[2][e], dv32[3][e]};
-            *(uint4 *)(Vt + (col + e) * LDV + pc) = w;
-            *(uint4 *)(dVt + (col + e) * LDV + pc) = dw;
-          }
-        }
-      }
-      __syncthreads();
+    for (int kc = 0; kc < BN / CK; ++kc) {
+      const int kb = kc * CK;               // first key of this step in the tile
 
-      // ---- S^T and dS^T for every 32-key sub-block ----
+      // ---- S^T and dS^T for every 32-key sub-block of the step ----
       f32x16 sacc[NSB], dsacc[NSB];
 #pragma unroll
       for (int sb = 0; sb < NSB; ++sb) {
         f32x16 s_ = f32x16{}, ds_ = f32x16{};
-        const T *krow = Ks + (sb * 32 + qi) * LDK + hl * KL;
-        const T *dkrow = dKs + (sb * 32 + qi) * LDK + hl * KL;
+        const int row = kb + sb * 32 + qi;
 #pragma unroll
         for (int s = 0; s < DS; ++s) {
-          const Frag kf = *(const Frag *)(krow + s * KI);
-          const Frag dkf = *(const Frag *)(dkrow + s * KI);
+          const int bcol = (s * KI + hl * KL) * (int)sizeof(T);
+          const Frag kf = *(const Frag *)(Ks + lds_off<RB>(row, bcol));
+          const Frag dkf = *(const Frag *)(dKs + lds_off<RB>(row, bcol));
           s_ = E::mfma(kf, qf[s], s_);
           ds_ = E::mfma(kf, dqf[s], ds_);
           ds_ = E::mfma(dkf, qf[s], ds_);
@@ -385,13 +402,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
       }
 
       // ---- masks: key tail and partial frame-window tiles ----
-      const bool tail = k0 + BN > N;
+      const int ka = k0 + kb;                // first key of the step
+      const bool tail = ka + CK > N;
       bool partial = false;
       if constexpr (MASKED) {
-        const int k1 = k0 + BN;
-        const bool in_win = k0 >= win_lo && k1 <= win_hi;
-        const bool in_first = p.mask.first && k1 <= p.mask.tpf;
-        const bool in_last = p.mask.last && k0 >= (p.mask.frames - 1) * p.mask.tpf;
+        const int kz = ka + CK;
+        const bool in_win = ka >= win_lo && kz <= win_hi;
+        const bool in_first = p.mask.first && kz <= p.mask.tpf;
+        const bool in_last = p.mask.last && ka >= (p.mask.frames - 1) * p.mask.tpf;
         partial = !(in_win || in_first || in_last);
       }
       if (tail || partial) {
@@ -399,13 +417,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
         for (int sb = 0; sb < NSB; ++sb) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = k0 + sb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+            const int key = ka + sb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
             bool vis = key < N;
             if constexpr (MASKED) {
               if (partial && vis && !q_all) {
                 const int kf_ = div_fix(key, p.mask.tpf, p.mask.inv_tpf);
-                const int kc = div_fix(kf_, p.mask.chunk, p.mask.inv_chunk);
-                const int dc = kc > q_chunk ? kc - q_chunk : q_chunk - kc;
+                const int kc_ = div_fix(kf_, p.mask.chunk, p.mask.inv_chunk);
+                const int dc = kc_ > q_chunk ? kc_ - q_chunk : q_chunk - kc_;
                 vis = dc <= p.mask.radius || (p.mask.first && kf_ == 0) ||
                       (p.mask.last && kf_ == p.mask.frames - 1);
               }
@@ -418,36 +436,37 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
         }
       }
 
-      // ---- online softmax (log2 domain) ----
+      // ---- online softmax (log2 domain, lazy rescale) ----
       float mx = -INFINITY;
 #pragma unroll
       for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * c2);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      float lsum = 0.f, rsum = 0.f;
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
+      if (__any(mx > m_run + kRescaleThreshold)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+        r_run *= alpha;
+#pragma unroll
+        for (int e = 0; e < ND; ++e) {
+          oacc[e] *= alpha;
+          tacc[e] *= alpha;
+        }
+        m_run = m_new;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 #pragma unroll
       for (int sb = 0; sb < NSB; ++sb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[sb][r], c2, -m_use));
           const float hv = pv * (dsacc[sb][r] * scale);
-          lsum += pv;
-          rsum += hv;
+          l_run += pv;
+          r_run += hv;
           sacc[sb][r] = pv;
           dsacc[sb][r] = hv;
         }
-      }
-      l_run = fmaf(l_run, alpha, lsum);
-      r_run = fmaf(r_run, alpha, rsum);
-      m_run = m_new;
-#pragma unroll
-      for (int e = 0; e < ND; ++e) {
-        oacc[e] *= alpha;
-        tacc[e] *= alpha;
       }
 
       // ---- O^T += V^T P^T ; T^T += dV^T P^T + V^T H^T ----
@@ -457,15 +476,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
         for (int j = 0; j < PS; ++j) {
           const Frag pf = E::pack(sacc[sb], j);
           const Frag hf = E::pack(dsacc[sb], j);
-          // register r = j*KL + i of lane half hl sits at physical column
-          // 16*(r/8) + 8*hl + r%8 of the 32-key sub-block
-          const int r0 = j * KL;
-          const int pc = sb * 32 + 16 * (r0 >> 3) + 8 * hl + (r0 & 7);
 #pragma unroll
           for (int e = 0; e < ND; ++e) {
-            const int drow = e * 32 + qi;
-            const Frag vf = *(const Frag *)(Vt + drow * LDV + pc);
-            const Frag dvf = *(const Frag *)(dVt + drow * LDV + pc);
+            Frag vf, dvf;
+            if constexpr (BF16) {
+              // lane (d = 32e + qi, half hl) needs keys 16j + 4hl + 0..3 and
+              // 16j + 8 + 4hl + 0..3 of this sub-block: two transpose reads
+              const int g = lane >> 4, i = lane & 15;
+              const int col = 32 * e + 16 * (g & 1) + 4 * (i & 3);
+              const int row0 = kb + sb * 32 + 16 * j + 4 * hl + (i >> 2);
+              const int o0 = lds_off<RB>(row0, col * 2);
+              const int o1 = lds_off<RB>(row0 + 8, col * 2);
+              const i16x4 v0 = lds_read_tr(Vs + o0), v1 = lds_read_tr(Vs + o1);
+              const i16x4 w0 = lds_read_tr(dVs + o0), w1 = lds_read_tr(dVs + o1);
+              vf = __builtin_bit_cast(Frag, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+              dvf = __builtin_bit_cast(Frag, __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7));
+            } else {
+              // float32: register j of lane half hl holds key 8(j/4) + 4hl + j%4
+              const int key = kb + sb * 32 + 8 * (j >> 2) + 4 * hl + (j & 3);
+              const int o = lds_off<RB>(key, (32 * e + qi) * 4);
+              vf = *(const Frag *)(Vs + o);
+              dvf = *(const Frag *)(dVs + o);
+            }
             oacc[e] = E::mfma(vf, pf, oacc[e]);
             tacc[e] = E::mfma(dvf, pf, tacc[e]);
             tacc[e] = E::mfma(vf, hf, tacc[e]);
@@ -510,6 +542,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
 // Host side.
 // ---------------------------------------------------------------------------
 constexpr int kBlockN = 64;
+#ifndef ATTN_JVP_CK
+#define ATTN_JVP_CK 32
+#endif
 
 struct Extent {
   uintptr_t lo, hi;
@@ -602,7 +637,7 @@ int check_args(const void *Q, const void *K, const void *V, const void *dQ,
 
 template <typename T, int D, bool MASKED>
 hipError_t launch(const Params &p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_jvp_kernel<T, D, kBlockN, MASKED>), dim3(grid),
+  hipLaunchKernelGGL((attn_jvp_kernel<T, D, kBlockN, ATTN_JVP_CK, MASKED>), dim3(grid),
                      dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
