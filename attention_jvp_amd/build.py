@@ -16,6 +16,9 @@ OUTPUT = os.path.join(HERE, "libattn_jvp.so")
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in ArchVGPRs: the online rescale multiplies them
+    # with VALU ops, and AGPR accumulators would be copied every iteration
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I" + os.path.join(ROOT, "include"),
 ]
 

@@ -206,36 +206,65 @@ __device__ inline i16x4 lds_read_tr(const char *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
 }
 
-// Issue the asynchronous global->LDS copies of one key tile (K, dK, V, dV)
-// into `stage`.  Each wave instruction fills 1 KiB of LDS contiguously, lane l
-// writing bytes [16 l, 16 l + 16); the lane picks the global chunk that the
-// swizzled layout puts there.  Rows past the end of the sequence re-read row
-// N-1 (their scores are masked to -inf and their tangents to 0).
+// Asynchronous global->LDS copies of key tiles (K, dK, V, dV).  Each wave
+// instruction fills 1 KiB of LDS contiguously, lane l writing bytes
+// [16 l, 16 l + 16); the lane picks the global chunk that the swizzled layout
+// puts there.  The per-lane byte offsets inside a tile are fixed, so they are
+// computed once; a tile then only moves the (scalar) base pointers.  Rows
+// past the end of the sequence re-read row N-1 (their scores are masked to
+// -inf and their tangents to 0).
 template <typename T, int D, int BN>
-__device__ inline void issue_tile(const T *const src[4], const int64_t stride[4],
-                                  int k0, int N, char *stage, int wave, int lane) {
-  constexpr int RB = D * (int)sizeof(T);
-  constexpr int CPR = RB / 16;
-  constexpr int EV = 16 / (int)sizeof(T);
-  constexpr int TILE = BN * RB;
-  constexpr int IPW = TILE / 1024 / kWaves;   // wave instructions per tensor
+struct TileCopier {
+  static constexpr int RB = D * (int)sizeof(T);
+  static constexpr int CPR = RB / 16;
+  static constexpr int TILE = BN * RB;
+  static constexpr int IPW = TILE / 1024 / kWaves;   // wave instructions per tensor
   static_assert(IPW * 1024 * kWaves == TILE, "tile must split over the waves");
-#pragma unroll
-  for (int i = 0; i < IPW; ++i) {
-    const int gi = wave * IPW + i;
-    const int s = gi * 64 + lane;
-    const int r = s / CPR;
-    const int c = (s % CPR) ^ swz<RB>(r);
-    int key = k0 + r;
-    key = key < N ? key : N - 1;
+
+  const char *base[4];      // byte base of K, dK, V, dV for this (b, h)
+  int64_t rstride[4];       // row stride in bytes
+  uint32_t rs_k, rs_v;      // the same, 32-bit (below 2^24, checked on the host)
+  uint32_t slot[IPW];       // (row << 16) | (swizzled chunk * 16) per lane
+  int wave;                 // wave index (uniform)
+
+  __device__ void init(const T *const src[4], const int64_t stride[4], int wave_, int lane) {
+    wave = wave_;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const T *g = src[t] + (int64_t)key * stride[t] + c * EV;
-      __builtin_amdgcn_global_load_lds((const void *)g,
-                                       (lds_void *)(stage + t * TILE + gi * 1024), 16, 0, 0);
+      base[t] = (const char *)src[t];
+      rstride[t] = stride[t] * (int64_t)sizeof(T);
+    }
+    rs_k = (uint32_t)rstride[0];
+    rs_v = (uint32_t)rstride[2];
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int s = (wave * IPW + i) * 64 + lane;
+      const int r = s / CPR;
+      const int c = (s % CPR) ^ swz<RB>(r);
+      slot[i] = ((uint32_t)r << 16) | (uint32_t)(c * 16);
     }
   }
-}
+
+  __device__ void issue(int k0, int N, char *stage) const {
+    const int valid = (N - k0 < BN ? N - k0 : BN) - 1;   // last real row
+    const char *tb[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) tb[t] = base[t] + (int64_t)k0 * rstride[t];
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      uint32_t r = slot[i] >> 16;
+      r = r < (uint32_t)valid ? r : (uint32_t)valid;
+      const uint32_t c16 = slot[i] & 0xffffu;
+      const uint32_t ok = __umul24(r, rs_k) + c16;
+      const uint32_t ov = __umul24(r, rs_v) + c16;
+      char *dst = stage + (wave * IPW + i) * 1024;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        __builtin_amdgcn_global_load_lds((const void *)(tb[t] + (t < 2 ? ok : ov)),
+                                         (lds_void *)(dst + t * TILE), 16, 0, 0);
+    }
+  }
+};
 
 __device__ inline void wait_vmem() {
   // s_waitcnt vmcnt(0): every global->LDS copy this wave issued has landed
@@ -277,7 +306,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int qi = lane & 31;
   const int hl = lane >> 5;
 
@@ -311,7 +340,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
   for (int i = 0; i < tr.n; ++i) ntile += tr.hi[i] - tr.lo[i];
 
   // first tile in flight before anything else
-  issue_tile<T, D, BN>(src, stride, tile_at(tr, 0) * BN, N, smem, wave, lane);
+  TileCopier<T, D, BN> copier;
+  copier.init(src, stride, wave, lane);
+  copier.issue(tile_at(tr, 0) * BN, N, smem);
 
   const int qrow = q0 + wave * kWaveRows + qi;
   const bool qvalid = qrow < N;
@@ -370,9 +401,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
     const char *st = smem + (it & 1) * STAGE;
     wait_vmem();
     __syncthreads();   // tile `it` landed; every wave is done with tile it-1
-    if (it + 1 < ntile)
-      issue_tile<T, D, BN>(src, stride, tile_at(tr, it + 1) * BN, N,
-                           smem + ((it + 1) & 1) * STAGE, wave, lane);
+    if (it + 1 < ntile) copier.issue(tile_at(tr, it + 1) * BN, N, smem + ((it + 1) & 1) * STAGE);
     const char *Ks = st;
     const char *dKs = st + TILE;
     const char *Vs = st + 2 * TILE;
@@ -612,6 +641,8 @@ int check_args(const void *Q, const void *K, const void *V, const void *dQ,
   for (int i = 0; i < 4; ++i)
     for (int j = 0; j < 3; ++j)
       if (all[i][j] < 0 || all[i][j] % align != 0) return ATTN_JVP_ESTRIDE;
+  // key-tile offsets use 24-bit row strides (in bytes)
+  if (L->k[2] * esize >= (1 << 24) || L->v[2] * esize >= (1 << 24)) return ATTN_JVP_ESTRIDE;
   const void *ptrs[8] = {Q, K, V, dQ, dK, dV, O, dO};
   for (int i = 0; i < 8; ++i)
     if ((uintptr_t)ptrs[i] % 16 != 0) return ATTN_JVP_ESTRIDE;
