@@ -46,41 +46,37 @@
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;                      // two waves per SIMD
 constexpr int kThreads = 64 * kWaves;
-constexpr int kWaveRows = 32;                  // query rows per wave
+constexpr int kWaveRows = 16;                  // query rows per wave
 constexpr int kBlockM = kWaves * kWaveRows;    // query rows per workgroup
 
 // ---------------------------------------------------------------------------
-// Element traits: operand fragment per lane for the 32x32 MFMA family.
+// Element traits: operand fragment per lane for the 16x16 MFMA family.  For
+// an operand tile with 16 rows (or columns) and K along the contraction, lane
+// l holds row l % 16 and the K slice of lane group l / 16; the 16x16 result
+// puts column l % 16 and rows 4 (l / 16) + 0..3 in lane l.
 // ---------------------------------------------------------------------------
 template <typename T> struct Elem;
 
 template <> struct Elem<__bf16> {
-  using Frag = bf16x8;            // 8 bf16 along k per lane
-  static constexpr int KL = 8;    // k elements per lane
-  static constexpr int KI = 16;   // k per instruction (two lane halves)
-  __device__ static inline f32x16 mfma(Frag a, Frag b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-  }
-  __device__ static inline Frag pack(const f32x16 &x, int j) {
-    Frag f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = (__bf16)x[j * 8 + e];
-    return f;
+  using Frag = bf16x8;            // 8 bf16 along K per lane
+  static constexpr int KL = 8;    // K elements per lane
+  static constexpr int KI = 32;   // K per instruction (four lane groups)
+  __device__ static inline f32x4 mfma(Frag a, Frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
 };
 
 template <> struct Elem<float> {
   using Frag = float;
   static constexpr int KL = 1;
-  static constexpr int KI = 2;
-  __device__ static inline f32x16 mfma(Frag a, Frag b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  static constexpr int KI = 4;
+  __device__ static inline f32x4 mfma(Frag a, Frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
   }
-  __device__ static inline Frag pack(const f32x16 &x, int j) { return x[j]; }
 };
 
 // ---------------------------------------------------------------------------
@@ -116,6 +112,7 @@ __host__ __device__ inline TileRanges visible_tiles(const MaskDev &m, int q_lo,
   tr.n = 1;
   tr.lo[0] = 0;
   tr.hi[0] = ntiles;
+  tr.lo[1] = tr.hi[1] = tr.lo[2] = tr.hi[2] = 0;
   if (m.kind == 0) return tr;
   const int T = m.tpf, C = m.chunk, F = m.frames, R = m.radius;
   const int qf0 = q_lo / T, qf1 = (q_hi - 1) / T;
@@ -177,16 +174,17 @@ __device__ inline int logical_block_id() {
 // LDS tile layout.  A K, dK, V or dV tile is BN rows of RB = d * sizeof(T)
 // bytes, row-major (one key per row).  The 16-byte chunks of row r are XOR
 // permuted with swz(r) so that (a) 16 consecutive rows read at one logical
-// chunk (the K operand) and (b) 4 consecutive rows read as a 64-byte run (the
-// transpose reads of V) both touch every bank once.
+// chunk (the K operand, 16 lanes per LDS pass) and (b) 8 consecutive rows
+// each read as a 32-byte run (the transpose reads of V, 32 lanes per pass)
+// both touch every bank once.
 // ---------------------------------------------------------------------------
 template <int RB>
 __device__ inline int swz(int r) {
   constexpr int CPR = RB / 16;            // chunks per row
   constexpr int RPB = 256 / RB;           // rows per 256-byte bank sweep
-  constexpr int Q = CPR / 4;
+  constexpr int H = CPR / 2;
   const int m = r / RPB;
-  return ((m % Q) << 2) | ((m / Q) % 4);
+  return ((m % H) << 1) | ((m / H) % 2);
 }
 
 template <int RB>
@@ -202,8 +200,26 @@ typedef __attribute__((address_space(3))) void lds_void;
 // Read 4 consecutive-key bf16 values of one d column: ds_read_b64_tr_b16.
 // In each 16-lane group, lane i receives element (i % 4) of the 8-byte chunks
 // addressed by lanes i/4, i/4 + 4, i/4 + 8 and i/4 + 12 (in that order).
+//
+// Issued through inline asm: the compiler cannot tell that these reads never
+// touch the LDS stage an in-flight global->LDS copy is filling, and would
+// otherwise wait for every outstanding copy (vmcnt(0)) before the first one,
+// serialising the tile prefetch.  The compiler does not count these reads, so
+// lds_tr_wait() must run before their results are used; extra LDS operations
+// it does not know about only make its own lgkmcnt waits stronger, since LDS
+// operations complete in issue order.
 __device__ inline i16x4 lds_read_tr(const char *p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
+  const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+  i16x4 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(a));
+  return v;
+}
+
+// Wait until at most N LDS operations are outstanding; the four values pass
+// through the asm so that nothing reading them can be scheduled before it.
+template <int N>
+__device__ inline void lds_tr_wait(i16x4 &a, i16x4 &b, i16x4 &c, i16x4 &d) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "n"(N));
 }
 
 // Asynchronous global->LDS copies of key tiles (K, dK, V, dV).  Each wave
@@ -297,18 +313,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
   constexpr int TILE = BN * RB;               // bytes per tensor tile
   constexpr int STAGE = 4 * TILE;             // K, dK, V, dV
   constexpr int DS = D / KI;                  // k-steps over d
-  constexpr int NSB = CK / 32;                // 32-key sub-blocks per softmax step
-  constexpr int ND = D / 32;                  // 32-wide d blocks
-  constexpr int PS = 32 / KI;                 // k-steps per sub-block (P V)
-  static_assert(CK % 32 == 0 && BN % CK == 0 && D % 32 == 0, "tile shape");
+  constexpr int ND = D / 16;                  // 16-wide d blocks
+  static_assert(CK == 32 && BN % CK == 0 && D % 32 == 0, "tile shape");
 
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
-  const int qi = lane & 31;
-  const int hl = lane >> 5;
+  const int qi = lane & 15;        // this lane's query within the wave
+  const int lg = lane >> 4;        // lane group 0..3
 
   const int lid = logical_block_id();
   const int bh = lid / p.nqb;
@@ -335,9 +349,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
     tr.n = 1;
     tr.lo[0] = 0;
     tr.hi[0] = (N + BN - 1) / BN;
+    tr.lo[1] = tr.hi[1] = tr.lo[2] = tr.hi[2] = 0;
   }
-  int ntile = 0;
-  for (int i = 0; i < tr.n; ++i) ntile += tr.hi[i] - tr.lo[i];
+  // unused ranges are empty (lo = hi = 0)
+  const int ntile = (tr.hi[0] - tr.lo[0]) + (tr.hi[1] - tr.lo[1]) + (tr.hi[2] - tr.lo[2]);
 
   // first tile in flight before anything else
   TileCopier<T, D, BN> copier;
@@ -352,7 +367,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
 #pragma unroll
   for (int s = 0; s < DS; ++s) {
     if (qvalid) {
-      const int64_t off = (int64_t)qrow * p.sq[2] + s * KI + hl * KL;
+      const int64_t off = (int64_t)qrow * p.sq[2] + s * KI + lg * KL;
       qf[s] = *(const Frag *)(Q + off);
       dqf[s] = *(const Frag *)(dQ + off);
     } else {
@@ -361,11 +376,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
     }
   }
 
-  f32x16 oacc[ND], tacc[ND];
+  // O^T and T^T blocks: lane holds d = 16e + 4 lg + 0..3 of query qi
+  f32x4 oacc[ND], tacc[ND];
 #pragma unroll
   for (int e = 0; e < ND; ++e) {
-    oacc[e] = f32x16{};
-    tacc[e] = f32x16{};
+    oacc[e] = f32x4{};
+    tacc[e] = f32x4{};
   }
   float m_run = -INFINITY;   // reference max, log2 units
   float l_run = 0.f;         // lane-partial sum of P~
@@ -411,23 +427,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
     for (int kc = 0; kc < BN / CK; ++kc) {
       const int kb = kc * CK;               // first key of this step in the tile
 
-      // ---- S^T and dS^T for every 32-key sub-block of the step ----
-      f32x16 sacc[NSB], dsacc[NSB];
+      // ---- S^T and dS^T for the two 16-key blocks of the step ----
+      // sacc[kb2][i] is the score of key kb + 16 kb2 + 4 lg + i for query qi
+      f32x4 sacc[2], dsacc[2];
 #pragma unroll
-      for (int sb = 0; sb < NSB; ++sb) {
-        f32x16 s_ = f32x16{}, ds_ = f32x16{};
-        const int row = kb + sb * 32 + qi;
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        f32x4 s_ = f32x4{}, ds_ = f32x4{};
+        const int row = kb + 16 * kb2 + qi;
 #pragma unroll
         for (int s = 0; s < DS; ++s) {
-          const int bcol = (s * KI + hl * KL) * (int)sizeof(T);
+          const int bcol = (s * KI + lg * KL) * (int)sizeof(T);
           const Frag kf = *(const Frag *)(Ks + lds_off<RB>(row, bcol));
           const Frag dkf = *(const Frag *)(dKs + lds_off<RB>(row, bcol));
           s_ = E::mfma(kf, qf[s], s_);
           ds_ = E::mfma(kf, dqf[s], ds_);
           ds_ = E::mfma(dkf, qf[s], ds_);
         }
-        sacc[sb] = s_;
-        dsacc[sb] = ds_;
+        sacc[kb2] = s_;
+        dsacc[kb2] = ds_;
       }
 
       // ---- masks: key tail and partial frame-window tiles ----
@@ -443,10 +460,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
       }
       if (tail || partial) {
 #pragma unroll
-        for (int sb = 0; sb < NSB; ++sb) {
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = ka + sb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          for (int i = 0; i < 4; ++i) {
+            const int key = ka + 16 * kb2 + 4 * lg + i;
             bool vis = key < N;
             if constexpr (MASKED) {
               if (partial && vis && !q_all) {
@@ -458,19 +475,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
               }
             }
             if (!vis) {
-              sacc[sb][r] = -INFINITY;
-              dsacc[sb][r] = 0.f;
+              sacc[kb2][i] = -INFINITY;
+              dsacc[kb2][i] = 0.f;
             }
           }
         }
       }
 
       // ---- online softmax (log2 domain, lazy rescale) ----
-      float mx = -INFINITY;
-#pragma unroll
-      for (int sb = 0; sb < NSB; ++sb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][r]);
+      float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
+                       fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
       if (__any(mx > m_run + kRescaleThreshold)) {
         const float m_new = fmaxf(m_run, mx);
@@ -486,59 +501,86 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
       }
       const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 #pragma unroll
-      for (int sb = 0; sb < NSB; ++sb) {
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[sb][r], c2, -m_use));
-          const float hv = pv * (dsacc[sb][r] * scale);
+        for (int i = 0; i < 4; ++i) {
+          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][i], c2, -m_use));
+          const float hv = pv * (dsacc[kb2][i] * scale);
           l_run += pv;
           r_run += hv;
-          sacc[sb][r] = pv;
-          dsacc[sb][r] = hv;
+          sacc[kb2][i] = pv;
+          dsacc[kb2][i] = hv;
         }
       }
 
       // ---- O^T += V^T P^T ; T^T += dV^T P^T + V^T H^T ----
+      if constexpr (BF16) {
+        // B operand: lane (query qi, group lg) gives keys 4lg + 0..3 and
+        // 16 + 4lg + 0..3 of the step, in that order
+        bf16x8 pf, hf;
 #pragma unroll
-      for (int sb = 0; sb < NSB; ++sb) {
-#pragma unroll
-        for (int j = 0; j < PS; ++j) {
-          const Frag pf = E::pack(sacc[sb], j);
-          const Frag hf = E::pack(dsacc[sb], j);
-#pragma unroll
-          for (int e = 0; e < ND; ++e) {
-            Frag vf, dvf;
-            if constexpr (BF16) {
-              // lane (d = 32e + qi, half hl) needs keys 16j + 4hl + 0..3 and
-              // 16j + 8 + 4hl + 0..3 of this sub-block: two transpose reads
-              const int g = lane >> 4, i = lane & 15;
-              const int col = 32 * e + 16 * (g & 1) + 4 * (i & 3);
-              const int row0 = kb + sb * 32 + 16 * j + 4 * hl + (i >> 2);
-              const int o0 = lds_off<RB>(row0, col * 2);
-              const int o1 = lds_off<RB>(row0 + 8, col * 2);
-              const i16x4 v0 = lds_read_tr(Vs + o0), v1 = lds_read_tr(Vs + o1);
-              const i16x4 w0 = lds_read_tr(dVs + o0), w1 = lds_read_tr(dVs + o1);
-              vf = __builtin_bit_cast(Frag, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-              dvf = __builtin_bit_cast(Frag, __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7));
-            } else {
-              // float32: register j of lane half hl holds key 8(j/4) + 4hl + j%4
-              const int key = kb + sb * 32 + 8 * (j >> 2) + 4 * hl + (j & 3);
-              const int o = lds_off<RB>(key, (32 * e + qi) * 4);
-              vf = *(const Frag *)(Vs + o);
-              dvf = *(const Frag *)(dVs + o);
-            }
-            oacc[e] = E::mfma(vf, pf, oacc[e]);
-            tacc[e] = E::mfma(dvf, pf, tacc[e]);
-            tacc[e] = E::mfma(vf, hf, tacc[e]);
-          }
+        for (int i = 0; i < 4; ++i) {
+          pf[i] = (__bf16)sacc[0][i];
+          pf[4 + i] = (__bf16)sacc[1][i];
+          hf[i] = (__bf16)dsacc[0][i];
+          hf[4 + i] = (__bf16)dsacc[1][i];
         }
+        // A operand for d block e: lane (d = 16e + qi, group lg) needs the
+        // same keys of V and dV -- four transpose reads.  Group e+1 is in
+        // flight while group e feeds its MFMAs.
+        auto issue = [&](int e, i16x4 (&r)[4]) {
+          const int col = 16 * e + 4 * (qi & 3);
+          const int row0 = kb + 4 * lg + (qi >> 2);
+          const int o0 = lds_off<RB>(row0, col * 2);
+          const int o1 = lds_off<RB>(row0 + 16, col * 2);
+          r[0] = lds_read_tr(Vs + o0);
+          r[1] = lds_read_tr(Vs + o1);
+          r[2] = lds_read_tr(dVs + o0);
+          r[3] = lds_read_tr(dVs + o1);
+        };
+        i16x4 buf[2][4];
+        issue(0, buf[0]);
+#pragma unroll
+        for (int e = 0; e < ND; ++e) {
+          i16x4(&cur)[4] = buf[e & 1];
+          if (e + 1 < ND) {
+            issue(e + 1, buf[(e + 1) & 1]);
+            lds_tr_wait<4>(cur[0], cur[1], cur[2], cur[3]);
+          } else {
+            lds_tr_wait<0>(cur[0], cur[1], cur[2], cur[3]);
+          }
+          const Frag vf = __builtin_bit_cast(Frag, __builtin_shufflevector(cur[0], cur[1], 0, 1, 2, 3, 4, 5, 6, 7));
+          const Frag dvf = __builtin_bit_cast(Frag, __builtin_shufflevector(cur[2], cur[3], 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[e] = E::mfma(vf, pf, oacc[e]);
+          tacc[e] = E::mfma(dvf, pf, tacc[e]);
+          tacc[e] = E::mfma(vf, hf, tacc[e]);
+        }
+      } else {
+        // float32: k-step (kb2, i) takes key 16 kb2 + 4 lg + i from lane group lg
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kb + 16 * kb2 + 4 * lg + i;
+#pragma unroll
+            for (int e = 0; e < ND; ++e) {
+              const int o = lds_off<RB>(key, (16 * e + qi) * 4);
+              const Frag vf = *(const Frag *)(Vs + o);
+              const Frag dvf = *(const Frag *)(dVs + o);
+              oacc[e] = E::mfma(vf, sacc[kb2][i], oacc[e]);
+              tacc[e] = E::mfma(dvf, sacc[kb2][i], tacc[e]);
+              tacc[e] = E::mfma(vf, dsacc[kb2][i], tacc[e]);
+            }
+          }
       }
     }
   }
 
   // ---- epilogue ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float r_tot = r_run + __shfl_xor(r_run, 32);
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  float r_tot = r_run + __shfl_xor(r_run, 16);
+  r_tot += __shfl_xor(r_tot, 32);
   const bool empty = !(l_tot > 0.f);
   const float inv = empty ? 0.f : 1.f / l_tot;
   const float mu = r_tot * inv;
@@ -547,19 +589,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
     T *dO = (T *)p.dout + b * p.so[0] + h * p.so[1] + (int64_t)qrow * p.so[2];
 #pragma unroll
     for (int e = 0; e < ND; ++e) {
+      const int d0 = 16 * e + 4 * lg;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = e * 32 + 8 * g + 4 * hl;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float o = oacc[e][4 * g + i] * inv;
-          const float dov = tacc[e][4 * g + i] * inv - mu * o;
-          O[d0 + i] = (T)o;
-          dO[d0 + i] = (T)dov;
-        }
+      for (int i = 0; i < 4; ++i) {
+        const float o = oacc[e][i] * inv;
+        const float dov = tacc[e][i] * inv - mu * o;
+        O[d0 + i] = (T)o;
+        dO[d0 + i] = (T)dov;
       }
     }
-    if (hl == 0) {
+    if (lg == 0) {
       const int64_t ro = (int64_t)bh * N + qrow;
       p.lse[ro] = empty ? -INFINITY : (m_run + log2f(l_tot)) * 0.69314718055994530942f;
       p.dlse[ro] = mu;

@@ -130,6 +130,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target length of the timed oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="instead of the benchmark, run --steps plain device copies of "
+                         "BYTES bytes (a known-size reference for HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -139,6 +142,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration // 4
+        src = torch.ones(n, device="cuda", dtype=torch.float32)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n * 4, "copies": args.steps}), flush=True)
+        return
 
     import attention_jvp_amd as aj
     from synth import WORKLOADS, make_inputs
