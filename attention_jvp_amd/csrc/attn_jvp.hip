@@ -222,6 +222,30 @@ __device__ inline void lds_tr_wait(i16x4 &a, i16x4 &b, i16x4 &c, i16x4 &d) {
   asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "n"(N));
 }
 
+// Reductions over the four lanes l, l^16, l^32, l^48 that hold one query
+// row.  v_permlane16_swap(x, x) returns rows (x0, x0, x2, x2) and
+// (x1, x1, x3, x3) of x's four 16-lane rows, and v_permlane32_swap(x, x)
+// returns halves (lo, lo) and (hi, hi): combining the pair is one butterfly
+// step, done in the VALU without an LDS round trip.  Every lane of the row
+// ends with the same bits (same operand order on both sides).
+__device__ inline float row_max4(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const unsigned v = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ inline float row_sum4(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const unsigned v = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Asynchronous global->LDS copies of key tiles (K, dK, V, dV).  Each wave
 // instruction fills 1 KiB of LDS contiguously, lane l writing bytes
 // [16 l, 16 l + 16); the lane picks the global chunk that the swizzled layout
@@ -485,8 +509,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
       // ---- online softmax (log2 domain, lazy rescale) ----
       float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
                        fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
+      mx = row_max4(mx) * c2;
       if (__any(mx > m_run + kRescaleThreshold)) {
         const float m_new = fmaxf(m_run, mx);
         const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -577,26 +600,29 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
   }
 
   // ---- epilogue ----
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  float r_tot = r_run + __shfl_xor(r_run, 16);
-  r_tot += __shfl_xor(r_tot, 32);
+  const float l_tot = row_sum4(l_run);
+  const float r_tot = row_sum4(r_run);
   const bool empty = !(l_tot > 0.f);
   const float inv = empty ? 0.f : 1.f / l_tot;
   const float mu = r_tot * inv;
   if (qvalid) {
     T *O = (T *)p.o + b * p.so[0] + h * p.so[1] + (int64_t)qrow * p.so[2];
     T *dO = (T *)p.dout + b * p.so[0] + h * p.so[1] + (int64_t)qrow * p.so[2];
+    // each lane owns 4 consecutive d of its row per d block: one packed
+    // 8-byte (bf16) or 16-byte (float32) store per block and tensor
+    typedef T T4 __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int e = 0; e < ND; ++e) {
       const int d0 = 16 * e + 4 * lg;
+      T4 ov, dv;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float o = oacc[e][i] * inv;
-        const float dov = tacc[e][i] * inv - mu * o;
-        O[d0 + i] = (T)o;
-        dO[d0 + i] = (T)dov;
+        ov[i] = (T)o;
+        dv[i] = (T)(tacc[e][i] * inv - mu * o);
       }
+      *(T4 *)(O + d0) = ov;
+      *(T4 *)(dO + d0) = dv;
     }
     if (lg == 0) {
       const int64_t ro = (int64_t)bh * N + qrow;
