@@ -41,6 +41,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "attn_jvp.h"
 
 namespace {
@@ -208,11 +210,25 @@ typedef __attribute__((address_space(3))) void lds_void;
 // lds_tr_wait() must run before their results are used; extra LDS operations
 // it does not know about only make its own lgkmcnt waits stronger, since LDS
 // operations complete in issue order.
-__device__ inline i16x4 lds_read_tr(const char *p) {
-  const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+template <int OFF>
+__device__ inline i16x4 lds_read_tr(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "DS offset field");
   i16x4 v;
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(a));
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
   return v;
+}
+
+__device__ inline uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ inline void static_for(F &&f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 // Wait until at most N LDS operations are outstanding; the four values pass
@@ -222,21 +238,29 @@ __device__ inline void lds_tr_wait(i16x4 &a, i16x4 &b, i16x4 &c, i16x4 &d) {
   asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "n"(N));
 }
 
-// Reductions over the four lanes l, l^16, l^32, l^48 that hold one query
-// row.  v_permlane16_swap(x, x) returns rows (x0, x0, x2, x2) and
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte LDS read of a K or dK operand, issued through inline asm for the
+// same reason as the transpose reads (and so that the reads of the next
+// k-step can be put in flight ahead of the current k-step's MFMAs).
+__device__ inline i32x4 lds_read_b128(const char *p) {
+  const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+  i32x4 v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(a));
+  return v;
+}
+
+template <int N>
+__device__ inline void lds_wait(i32x4 &a, i32x4 &b, i32x4 &c, i32x4 &d) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "n"(N));
+}
+
+// Sum and maximum over the four lanes l, l^16, l^32, l^48 that hold one
+// query row.  v_permlane16_swap(x, x) returns rows (x0, x0, x2, x2) and
 // (x1, x1, x3, x3) of x's four 16-lane rows, and v_permlane32_swap(x, x)
 // returns halves (lo, lo) and (hi, hi): combining the pair is one butterfly
 // step, done in the VALU without an LDS round trip.  Every lane of the row
 // ends with the same bits (same operand order on both sides).
-__device__ inline float row_max4(float x) {
-  const unsigned u = __float_as_uint(x);
-  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const unsigned v = __float_as_uint(x);
-  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
 __device__ inline float row_sum4(float x) {
   const unsigned u = __float_as_uint(x);
   const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
@@ -244,6 +268,15 @@ __device__ inline float row_sum4(float x) {
   const unsigned v = __float_as_uint(x);
   const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ inline float row_max4(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const unsigned v = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // Asynchronous global->LDS copies of key tiles (K, dK, V, dV).  Each wave
@@ -285,7 +318,8 @@ struct TileCopier {
     }
   }
 
-  __device__ void issue(int k0, int N, char *stage) const {
+  // LDS layout: tensor t, stage g at smem + (2 t + g) TILE
+  __device__ void issue(int k0, int N, char *smem, int g) const {
     const int valid = (N - k0 < BN ? N - k0 : BN) - 1;   // last real row
     const char *tb[4];
 #pragma unroll
@@ -297,11 +331,11 @@ struct TileCopier {
       const uint32_t c16 = slot[i] & 0xffffu;
       const uint32_t ok = __umul24(r, rs_k) + c16;
       const uint32_t ov = __umul24(r, rs_v) + c16;
-      char *dst = stage + (wave * IPW + i) * 1024;
+      char *dst = smem + g * TILE + (wave * IPW + i) * 1024;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         __builtin_amdgcn_global_load_lds((const void *)(tb[t] + (t < 2 ? ok : ov)),
-                                         (lds_void *)(dst + t * TILE), 16, 0, 0);
+                                         (lds_void *)(dst + 2 * t * TILE), 16, 0, 0);
     }
   }
 };
@@ -381,7 +415,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
   // first tile in flight before anything else
   TileCopier<T, D, BN> copier;
   copier.init(src, stride, wave, lane);
-  copier.issue(tile_at(tr, 0) * BN, N, smem);
+  copier.issue(tile_at(tr, 0) * BN, N, smem, 0);
 
   const int qrow = q0 + wave * kWaveRows + qi;
   const bool qvalid = qrow < N;
@@ -401,15 +435,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
   }
 
   // O^T and T^T blocks: lane holds d = 16e + 4 lg + 0..3 of query qi
-  f32x4 oacc[ND], tacc[ND];
+  // O^T, A^T = (P~ dV)^T and B^T = ((P~ . dS) V)^T blocks (dS without the
+  // scale, applied once in the epilogue): lane holds d = 16e + 4 lg + 0..3 of
+  // query qi.  The row sums l (of P~) and r (of P~ . dS) are taken in fp32
+  // before the bf16 rounding, lane-partial until the epilogue.
+  f32x4 oacc[ND], aacc[ND], bacc[ND];
 #pragma unroll
   for (int e = 0; e < ND; ++e) {
     oacc[e] = f32x4{};
-    tacc[e] = f32x4{};
+    aacc[e] = f32x4{};
+    bacc[e] = f32x4{};
   }
+  float l_run = 0.f, r_run = 0.f;
   float m_run = -INFINITY;   // reference max, log2 units
-  float l_run = 0.f;         // lane-partial sum of P~
-  float r_run = 0.f;         // lane-partial sum of H~
 
   const float scale = p.scale;
   const float c2 = p.scale_log2;
@@ -436,175 +474,203 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
     }
   }
 
-  for (int it = 0; it < ntile; ++it) {
-    const int k0 = tile_at(tr, it) * BN;
-    const char *st = smem + (it & 1) * STAGE;
-    wait_vmem();
-    __syncthreads();   // tile `it` landed; every wave is done with tile it-1
-    if (it + 1 < ntile) copier.issue(tile_at(tr, it + 1) * BN, N, smem + ((it + 1) & 1) * STAGE);
-    const char *Ks = st;
-    const char *dKs = st + TILE;
-    const char *Vs = st + 2 * TILE;
-    const char *dVs = st + 3 * TILE;
+  // Lane-dependent parts of the LDS addresses, fixed for the whole loop.
+  // Rows kb + 16 kb2 + qi (K operand) and kb + 16 u + 4 lg + qi / 4
+  // (transpose reads of V) have the swizzle of their row mod 16, so adding
+  // the step's row offset and the stage/tensor offset is a constant that goes
+  // into the instructions' offset field.
+  const uint32_t smem_a = lds_addr(smem);
+  uint32_t kl[DS];                          // K operand, k-step s
+#pragma unroll
+  for (int s = 0; s < DS; ++s) kl[s] = smem_a + lds_off<RB>(qi, (s * KI + lg * KL) * (int)sizeof(T));
+  uint32_t vl[BF16 ? ND : 1];               // V transpose reads, d block e
+  if constexpr (BF16) {
+#pragma unroll
+    for (int e = 0; e < ND; ++e)
+      vl[e] = smem_a + 4 * TILE + lds_off<RB>(4 * lg + (qi >> 2), (16 * e + 4 * (qi & 3)) * 2);
+  }
 
-#pragma unroll
-    for (int kc = 0; kc < BN / CK; ++kc) {
-      const int kb = kc * CK;               // first key of this step in the tile
+  // One 32-key step (kc) of the tile in stage G.
+  auto step = [&](auto G_, auto KC_, int k0) {
+    constexpr int G = decltype(G_)::value;
+    constexpr int KC = decltype(KC_)::value;
+    constexpr int kb = KC * CK;                     // first key of the step in the tile
 
-      // ---- S^T and dS^T for the two 16-key blocks of the step ----
-      // sacc[kb2][i] is the score of key kb + 16 kb2 + 4 lg + i for query qi
-      f32x4 sacc[2], dsacc[2];
+    // ---- S^T and dS^T for the two 16-key blocks of the step ----
+    // sacc[kb2][i] is the score of key kb + 16 kb2 + 4 lg + i for query qi
+    f32x4 sacc[2], dsacc[2];
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        f32x4 s_ = f32x4{}, ds_ = f32x4{};
-        const int row = kb + 16 * kb2 + qi;
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      f32x4 s_ = f32x4{}, ds_ = f32x4{};
 #pragma unroll
-        for (int s = 0; s < DS; ++s) {
-          const int bcol = (s * KI + lg * KL) * (int)sizeof(T);
-          const Frag kf = *(const Frag *)(Ks + lds_off<RB>(row, bcol));
-          const Frag dkf = *(const Frag *)(dKs + lds_off<RB>(row, bcol));
-          s_ = E::mfma(kf, qf[s], s_);
-          ds_ = E::mfma(kf, dqf[s], ds_);
-          ds_ = E::mfma(dkf, qf[s], ds_);
-        }
-        sacc[kb2] = s_;
-        dsacc[kb2] = ds_;
+      for (int s = 0; s < DS; ++s) {
+        const char *kp = smem + (kl[s] - smem_a) + G * TILE + (kb + 16 * kb2) * RB;
+        const Frag kf = *(const Frag *)kp;
+        const Frag dkf = *(const Frag *)(kp + 2 * TILE);
+        s_ = E::mfma(kf, qf[s], s_);
+        ds_ = E::mfma(kf, dqf[s], ds_);
+        ds_ = E::mfma(dkf, qf[s], ds_);
       }
+      sacc[kb2] = s_;
+      dsacc[kb2] = ds_;
+    }
 
-      // ---- masks: key tail and partial frame-window tiles ----
-      const int ka = k0 + kb;                // first key of the step
-      const bool tail = ka + CK > N;
-      bool partial = false;
-      if constexpr (MASKED) {
-        const int kz = ka + CK;
-        const bool in_win = ka >= win_lo && kz <= win_hi;
-        const bool in_first = p.mask.first && kz <= p.mask.tpf;
-        const bool in_last = p.mask.last && ka >= (p.mask.frames - 1) * p.mask.tpf;
-        partial = !(in_win || in_first || in_last);
-      }
-      if (tail || partial) {
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = ka + 16 * kb2 + 4 * lg + i;
-            bool vis = key < N;
-            if constexpr (MASKED) {
-              if (partial && vis && !q_all) {
-                const int kf_ = div_fix(key, p.mask.tpf, p.mask.inv_tpf);
-                const int kc_ = div_fix(kf_, p.mask.chunk, p.mask.inv_chunk);
-                const int dc = kc_ > q_chunk ? kc_ - q_chunk : q_chunk - kc_;
-                vis = dc <= p.mask.radius || (p.mask.first && kf_ == 0) ||
-                      (p.mask.last && kf_ == p.mask.frames - 1);
-              }
-            }
-            if (!vis) {
-              sacc[kb2][i] = -INFINITY;
-              dsacc[kb2][i] = 0.f;
-            }
-          }
-        }
-      }
-
-      // ---- online softmax (log2 domain, lazy rescale) ----
-      float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
-                       fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
-      mx = row_max4(mx) * c2;
-      if (__any(mx > m_run + kRescaleThreshold)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-        r_run *= alpha;
-#pragma unroll
-        for (int e = 0; e < ND; ++e) {
-          oacc[e] *= alpha;
-          tacc[e] *= alpha;
-        }
-        m_run = m_new;
-      }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    // ---- masks: key tail and partial frame-window tiles ----
+    const int ka = k0 + kb;                // first key of the step
+    const bool tail = ka + CK > N;
+    bool partial = false;
+    if constexpr (MASKED) {
+      const int kz = ka + CK;
+      const bool in_win = ka >= win_lo && kz <= win_hi;
+      const bool in_first = p.mask.first && kz <= p.mask.tpf;
+      const bool in_last = p.mask.last && ka >= (p.mask.frames - 1) * p.mask.tpf;
+      partial = !(in_win || in_first || in_last);
+    }
+    if (tail || partial) {
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][i], c2, -m_use));
-          const float hv = pv * (dsacc[kb2][i] * scale);
-          l_run += pv;
-          r_run += hv;
-          sacc[kb2][i] = pv;
-          dsacc[kb2][i] = hv;
-        }
-      }
-
-      // ---- O^T += V^T P^T ; T^T += dV^T P^T + V^T H^T ----
-      if constexpr (BF16) {
-        // B operand: lane (query qi, group lg) gives keys 4lg + 0..3 and
-        // 16 + 4lg + 0..3 of the step, in that order
-        bf16x8 pf, hf;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pf[i] = (__bf16)sacc[0][i];
-          pf[4 + i] = (__bf16)sacc[1][i];
-          hf[i] = (__bf16)dsacc[0][i];
-          hf[4 + i] = (__bf16)dsacc[1][i];
-        }
-        // A operand for d block e: lane (d = 16e + qi, group lg) needs the
-        // same keys of V and dV -- four transpose reads.  Group e+1 is in
-        // flight while group e feeds its MFMAs.
-        auto issue = [&](int e, i16x4 (&r)[4]) {
-          const int col = 16 * e + 4 * (qi & 3);
-          const int row0 = kb + 4 * lg + (qi >> 2);
-          const int o0 = lds_off<RB>(row0, col * 2);
-          const int o1 = lds_off<RB>(row0 + 16, col * 2);
-          r[0] = lds_read_tr(Vs + o0);
-          r[1] = lds_read_tr(Vs + o1);
-          r[2] = lds_read_tr(dVs + o0);
-          r[3] = lds_read_tr(dVs + o1);
-        };
-        i16x4 buf[2][4];
-        issue(0, buf[0]);
-#pragma unroll
-        for (int e = 0; e < ND; ++e) {
-          i16x4(&cur)[4] = buf[e & 1];
-          if (e + 1 < ND) {
-            issue(e + 1, buf[(e + 1) & 1]);
-            lds_tr_wait<4>(cur[0], cur[1], cur[2], cur[3]);
-          } else {
-            lds_tr_wait<0>(cur[0], cur[1], cur[2], cur[3]);
-          }
-          const Frag vf = __builtin_bit_cast(Frag, __builtin_shufflevector(cur[0], cur[1], 0, 1, 2, 3, 4, 5, 6, 7));
-          const Frag dvf = __builtin_bit_cast(Frag, __builtin_shufflevector(cur[2], cur[3], 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[e] = E::mfma(vf, pf, oacc[e]);
-          tacc[e] = E::mfma(dvf, pf, tacc[e]);
-          tacc[e] = E::mfma(vf, hf, tacc[e]);
-        }
-      } else {
-        // float32: k-step (kb2, i) takes key 16 kb2 + 4 lg + i from lane group lg
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = kb + 16 * kb2 + 4 * lg + i;
-#pragma unroll
-            for (int e = 0; e < ND; ++e) {
-              const int o = lds_off<RB>(key, (16 * e + qi) * 4);
-              const Frag vf = *(const Frag *)(Vs + o);
-              const Frag dvf = *(const Frag *)(dVs + o);
-              oacc[e] = E::mfma(vf, sacc[kb2][i], oacc[e]);
-              tacc[e] = E::mfma(dvf, sacc[kb2][i], tacc[e]);
-              tacc[e] = E::mfma(vf, dsacc[kb2][i], tacc[e]);
+          const int key = ka + 16 * kb2 + 4 * lg + i;
+          bool vis = key < N;
+          if constexpr (MASKED) {
+            if (partial && vis && !q_all) {
+              const int kf_ = div_fix(key, p.mask.tpf, p.mask.inv_tpf);
+              const int kc_ = div_fix(kf_, p.mask.chunk, p.mask.inv_chunk);
+              const int dc = kc_ > q_chunk ? kc_ - q_chunk : q_chunk - kc_;
+              vis = dc <= p.mask.radius || (p.mask.first && kf_ == 0) ||
+                    (p.mask.last && kf_ == p.mask.frames - 1);
             }
           }
+          if (!vis) {
+            sacc[kb2][i] = -INFINITY;
+            dsacc[kb2][i] = 0.f;
+          }
+        }
       }
     }
+
+    // ---- online softmax (log2 domain, lazy rescale) ----
+    // IEEE maximum (NaN-propagating): v_maximum3_f32, no canonicalisation
+    const f32x4 m2 = __builtin_elementwise_maximum(sacc[0], sacc[1]);
+    float mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m2[0], m2[1]),
+                                             __builtin_elementwise_maximum(m2[2], m2[3]));
+    mx = row_max4(mx) * c2;
+    if (__any(mx > m_run + kRescaleThreshold)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+      r_run *= alpha;
+#pragma unroll
+      for (int e = 0; e < ND; ++e) {
+        oacc[e] *= alpha;
+        aacc[e] *= alpha;
+        bacc[e] *= alpha;
+      }
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][i], c2, -m_use));
+        const float hv = pv * dsacc[kb2][i];
+        l_run += pv;
+        r_run += hv;
+        sacc[kb2][i] = pv;
+        dsacc[kb2][i] = hv;
+      }
+    }
+
+    // ---- O^T += V^T P^T ; T^T += dV^T P^T + V^T H^T ----
+    if constexpr (BF16) {
+      // B operand: lane (query qi, group lg) gives keys 4lg + 0..3 and
+      // 16 + 4lg + 0..3 of the step, in that order
+      bf16x8 pf, hf;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pf[i] = (__bf16)sacc[0][i];
+        pf[4 + i] = (__bf16)sacc[1][i];
+        hf[i] = (__bf16)dsacc[0][i];
+        hf[4 + i] = (__bf16)dsacc[1][i];
+      }
+      // A operand for d block e: lane (d = 16e + qi, group lg) needs the same
+      // keys of V and dV -- four transpose reads.  Groups e+1 and e+2 are in
+      // flight while group e feeds its MFMAs.
+      constexpr int VO = G * TILE + kb * RB;          // stage and step rows
+      auto issue = [&](auto e_, i16x4 (&r)[4]) {
+        constexpr int e = decltype(e_)::value;
+        r[0] = lds_read_tr<VO>(vl[e]);
+        r[1] = lds_read_tr<VO + 16 * RB>(vl[e]);
+        r[2] = lds_read_tr<VO + 2 * TILE>(vl[e]);
+        r[3] = lds_read_tr<VO + 2 * TILE + 16 * RB>(vl[e]);
+      };
+      i16x4 buf[3][4];
+      issue(std::integral_constant<int, 0>{}, buf[0]);
+      if constexpr (ND > 1) issue(std::integral_constant<int, 1>{}, buf[1]);
+      static_for<0, ND>([&](auto e_) {
+        constexpr int e = decltype(e_)::value;
+        i16x4(&cur)[4] = buf[e % 3];
+        if constexpr (e + 2 < ND) {
+          issue(std::integral_constant<int, e + 2>{}, buf[(e + 2) % 3]);
+          lds_tr_wait<8>(cur[0], cur[1], cur[2], cur[3]);
+        } else if constexpr (e + 1 < ND) {
+          lds_tr_wait<4>(cur[0], cur[1], cur[2], cur[3]);
+        } else {
+          lds_tr_wait<0>(cur[0], cur[1], cur[2], cur[3]);
+        }
+        const Frag vf = __builtin_bit_cast(Frag, __builtin_shufflevector(cur[0], cur[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        const Frag dvf = __builtin_bit_cast(Frag, __builtin_shufflevector(cur[2], cur[3], 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[e] = E::mfma(vf, pf, oacc[e]);
+        aacc[e] = E::mfma(dvf, pf, aacc[e]);
+        bacc[e] = E::mfma(vf, hf, bacc[e]);
+      });
+    } else {
+      // float32: k-step (kb2, i) takes key 16 kb2 + 4 lg + i from lane group lg
+      const char *Vs = smem + 4 * TILE + G * TILE;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kb + 16 * kb2 + 4 * lg + i;
+#pragma unroll
+          for (int e = 0; e < ND; ++e) {
+            const int o = lds_off<RB>(key, (16 * e + qi) * 4);
+            const Frag vf = *(const Frag *)(Vs + o);
+            const Frag dvf = *(const Frag *)(Vs + 2 * TILE + o);
+            oacc[e] = E::mfma(vf, sacc[kb2][i], oacc[e]);
+            aacc[e] = E::mfma(dvf, sacc[kb2][i], aacc[e]);
+            bacc[e] = E::mfma(vf, dsacc[kb2][i], bacc[e]);
+          }
+        }
+    }
+  };
+
+  // One tile in stage G: wait for it, release the other stage to the copy of
+  // the next tile, then its 32-key steps.
+  auto tile = [&](auto G_, int it) {
+    constexpr int G = decltype(G_)::value;
+    const int k0 = tile_at(tr, it) * BN;
+    wait_vmem();
+    __syncthreads();   // tile `it` landed; every wave is done with tile it-1
+    if (it + 1 < ntile) copier.issue(tile_at(tr, it + 1) * BN, N, smem, 1 - G);
+    static_for<0, BN / CK>([&](auto kc) { step(G_, kc, k0); });
+  };
+
+  int it = 0;
+  for (; it + 1 < ntile; it += 2) {
+    tile(std::integral_constant<int, 0>{}, it);
+    tile(std::integral_constant<int, 1>{}, it + 1);
   }
+  if (it < ntile) tile(std::integral_constant<int, 0>{}, it);
 
   // ---- epilogue ----
   const float l_tot = row_sum4(l_run);
-  const float r_tot = row_sum4(r_run);
   const bool empty = !(l_tot > 0.f);
   const float inv = empty ? 0.f : 1.f / l_tot;
-  const float mu = r_tot * inv;
+  const float mu = scale * row_sum4(r_run) * inv;   // dLSE
+  const float sinv = scale * inv;
   if (qvalid) {
     T *O = (T *)p.o + b * p.so[0] + h * p.so[1] + (int64_t)qrow * p.so[2];
     T *dO = (T *)p.dout + b * p.so[0] + h * p.so[1] + (int64_t)qrow * p.so[2];
@@ -619,7 +685,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
       for (int i = 0; i < 4; ++i) {
         const float o = oacc[e][i] * inv;
         ov[i] = (T)o;
-        dv[i] = (T)(tacc[e][i] * inv - mu * o);
+        dv[i] = (T)(fmaf(bacc[e][i], sinv, aacc[e][i] * inv) - mu * o);
       }
       *(T4 *)(O + d0) = ov;
       *(T4 *)(dO + d0) = dv;
