@@ -102,9 +102,13 @@ def cpu_baseline(w, x, target_s):
         attention_jvp_rows(*arrs, rows, visible=vis)
         return time.perf_counter() - t0, rows
 
-    dt, _ = run(16)                                    # calibration
-    per_row = dt / 16
-    nrows = int(max(16, min(w.N, target_s / max(per_row, 1e-9))))
+    # calibrate t(n) = fixed + n * per_row from two short runs (the fixed
+    # part is the per-head widening of K, V, dK, dV to float64)
+    t16, _ = run(16)
+    t64, _ = run(64)
+    per_row = max((t64 - t16) / 48, 1e-9)
+    fixed = max(t16 - 16 * per_row, 0.0)
+    nrows = int(max(16, min(w.N, (target_s - fixed) / per_row)))
     dt, rows = run(nrows)
     if vis is None:
         pairs = len(rows) * w.N
