@@ -175,23 +175,37 @@ __device__ inline int logical_block_id() {
 // ---------------------------------------------------------------------------
 // LDS tile layout.  A K, dK, V or dV tile is BN rows of RB = d * sizeof(T)
 // bytes, row-major (one key per row).  The 16-byte chunks of row r are XOR
-// permuted with swz(r) so that (a) 16 consecutive rows read at one logical
-// chunk (the K operand, 16 lanes per LDS pass) and (b) 8 consecutive rows
-// each read as a 32-byte run (the transpose reads of V, 32 lanes per pass)
-// both touch every bank once.
+// permuted, with one rule for the tiles read as MFMA operand rows (K, dK) and
+// another for the tiles read by transposing loads (V, dV):
+//  * K side, kswz(r): the sweep index r / (256 / RB) of the row, mod the
+//    chunks per row.  16 consecutive rows read at one logical chunk then fill
+//    every 16-byte slot of a 256-byte bank sweep once, and the rows two
+//    lane groups read at neighbouring chunks stay apart as well.
+//  * V side, vswz(r): 8 consecutive rows, each read as a 32-byte run by four
+//    lanes of a transpose load, touch every bank once.
+// Both rules repeat every 16 rows, so a row offset that is a multiple of 16
+// keeps a lane's swizzle.
 // ---------------------------------------------------------------------------
 template <int RB>
-__device__ inline int swz(int r) {
+__device__ inline int kswz(int r) {
   constexpr int CPR = RB / 16;            // chunks per row
   constexpr int RPB = 256 / RB;           // rows per 256-byte bank sweep
+  return (r / RPB) % CPR;
+}
+
+template <int RB>
+__device__ inline int vswz(int r) {
+  constexpr int CPR = RB / 16;
+  constexpr int RPB = 256 / RB;
   constexpr int H = CPR / 2;
   const int m = r / RPB;
   return ((m % H) << 1) | ((m / H) % 2);
 }
 
-template <int RB>
+template <int RB, bool KSIDE>
 __device__ inline int lds_off(int r, int byte_col) {
-  return r * RB + ((((byte_col >> 4) ^ swz<RB>(r))) << 4) + (byte_col & 15);
+  const int x = KSIDE ? kswz<RB>(r) : vswz<RB>(r);
+  return r * RB + ((((byte_col >> 4) ^ x)) << 4) + (byte_col & 15);
 }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -297,7 +311,7 @@ struct TileCopier {
   const char *base[4];      // byte base of K, dK, V, dV for this (b, h)
   int64_t rstride[4];       // row stride in bytes
   uint32_t rs_k, rs_v;      // the same, 32-bit (below 2^24, checked on the host)
-  uint32_t slot[IPW];       // (row << 16) | (swizzled chunk * 16) per lane
+  uint32_t slot[IPW];       // (row << 16) | (K-side chunk * 16) << 8 | V-side chunk * 16
   int wave;                 // wave index (uniform)
 
   __device__ void init(const T *const src[4], const int64_t stride[4], int wave_, int lane) {
@@ -313,8 +327,9 @@ struct TileCopier {
     for (int i = 0; i < IPW; ++i) {
       const int s = (wave * IPW + i) * 64 + lane;
       const int r = s / CPR;
-      const int c = (s % CPR) ^ swz<RB>(r);
-      slot[i] = ((uint32_t)r << 16) | (uint32_t)(c * 16);
+      const int ck = (s % CPR) ^ kswz<RB>(r);
+      const int cv = (s % CPR) ^ vswz<RB>(r);
+      slot[i] = ((uint32_t)r << 16) | (uint32_t)(ck * 16) << 8 | (uint32_t)(cv * 16);
     }
   }
 
@@ -328,9 +343,8 @@ struct TileCopier {
     for (int i = 0; i < IPW; ++i) {
       uint32_t r = slot[i] >> 16;
       r = r < (uint32_t)valid ? r : (uint32_t)valid;
-      const uint32_t c16 = slot[i] & 0xffffu;
-      const uint32_t ok = __umul24(r, rs_k) + c16;
-      const uint32_t ov = __umul24(r, rs_v) + c16;
+      const uint32_t ok = __umul24(r, rs_k) + ((slot[i] >> 8) & 0xffu);
+      const uint32_t ov = __umul24(r, rs_v) + (slot[i] & 0xffu);
       char *dst = smem + g * TILE + (wave * IPW + i) * 1024;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
@@ -482,12 +496,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
   const uint32_t smem_a = lds_addr(smem);
   uint32_t kl[DS];                          // K operand, k-step s
 #pragma unroll
-  for (int s = 0; s < DS; ++s) kl[s] = smem_a + lds_off<RB>(qi, (s * KI + lg * KL) * (int)sizeof(T));
+  for (int s = 0; s < DS; ++s) kl[s] = smem_a + lds_off<RB, true>(qi, (s * KI + lg * KL) * (int)sizeof(T));
   uint32_t vl[BF16 ? ND : 1];               // V transpose reads, d block e
   if constexpr (BF16) {
 #pragma unroll
     for (int e = 0; e < ND; ++e)
-      vl[e] = smem_a + 4 * TILE + lds_off<RB>(4 * lg + (qi >> 2), (16 * e + 4 * (qi & 3)) * 2);
+      vl[e] = smem_a + 4 * TILE + lds_off<RB, false>(4 * lg + (qi >> 2), (16 * e + 4 * (qi & 3)) * 2);
   }
 
   // One 32-key step (kc) of the tile in stage G.
@@ -636,7 +650,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
           const int key = kb + 16 * kb2 + 4 * lg + i;
 #pragma unroll
           for (int e = 0; e < ND; ++e) {
-            const int o = lds_off<RB>(key, (16 * e + qi) * 4);
+            const int o = lds_off<RB, false>(key, (16 * e + qi) * 4);
             const Frag vf = *(const Frag *)(Vs + o);
             const Frag dvf = *(const Frag *)(Vs + 2 * TILE + o);
             oacc[e] = E::mfma(vf, sacc[kb2][i], oacc[e]);
