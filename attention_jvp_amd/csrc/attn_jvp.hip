@@ -238,7 +238,7 @@ __device__ inline uint32_t lds_addr(const void *p) {
 
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
 template <int B, int E, typename F>
-__device__ inline void static_for(F &&f) {
+__device__ __attribute__((always_inline)) inline void static_for(F &&f) {
   if constexpr (B < E) {
     f(std::integral_constant<int, B>{});
     static_for<B + 1, E>(f);
@@ -466,25 +466,37 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
   const float scale = p.scale;
   const float c2 = p.scale_log2;
 
-  // query-side mask terms; keys in [win_lo, win_hi) and the anchor frames are
-  // visible to every row of this block, so tiles inside them need no mask
-  int q_chunk = 0;
-  bool q_all = false;
+  // Query-side mask terms.  Chunks are runs of whole frames, so the keys
+  // this lane's query sees by the chunk rule form one interval
+  // [kv_lo, kv_hi); the anchor frames add [0, a_first_hi) and
+  // [a_last_lo, N).  Keys in [win_lo, win_hi) and the anchor frames are
+  // visible to every row of the block, so tiles inside them need no mask.
+  int kv_lo = 0, kv_hi = N, a_first_hi = 0, a_last_lo = N;
   int win_lo = 0, win_hi = 0;
   if constexpr (MASKED) {
+    const long long F = p.mask.frames, TPF = p.mask.tpf, C = p.mask.chunk, R = p.mask.radius;
     const int qf_ = div_fix(qvalid ? qrow : 0, p.mask.tpf, p.mask.inv_tpf);
-    q_chunk = div_fix(qf_, p.mask.chunk, p.mask.inv_chunk);
-    q_all = p.mask.see_all &&
-            ((p.mask.first && qf_ == 0) || (p.mask.last && qf_ == p.mask.frames - 1));
-    const int c0 = (q0 / p.mask.tpf) / p.mask.chunk;
-    const int c1 = ((q_hi - 1) / p.mask.tpf) / p.mask.chunk;
-    int flo = (c1 - p.mask.radius) * p.mask.chunk;
-    long long fhi = (long long)(c0 + p.mask.radius + 1) * p.mask.chunk;
-    if (flo < 0) flo = 0;
-    if (fhi > p.mask.frames) fhi = p.mask.frames;
-    if (fhi > flo) {
-      win_lo = flo * p.mask.tpf;
-      win_hi = (int)fhi * p.mask.tpf;
+    const int q_chunk = div_fix(qf_, p.mask.chunk, p.mask.inv_chunk);
+    const bool q_all = p.mask.see_all &&
+                       ((p.mask.first && qf_ == 0) || (p.mask.last && qf_ == p.mask.frames - 1));
+    long long flo = (q_chunk - R) * C, fhi = (q_chunk + R + 1) * C;
+    flo = flo < 0 ? 0 : flo;
+    fhi = fhi > F ? F : fhi;
+    if (!q_all) {
+      kv_lo = (int)(flo * TPF);
+      kv_hi = fhi > flo ? (int)(fhi * TPF) : kv_lo;
+    }
+    a_first_hi = p.mask.first ? (int)TPF : 0;
+    a_last_lo = p.mask.last ? (int)((F - 1) * TPF) : N;
+    // the rows of the whole block: chunks c0..c1
+    const long long c0 = (q0 / TPF) / C;
+    const long long c1 = ((q_hi - 1) / TPF) / C;
+    long long wlo = (c1 - R) * C, whi = (c0 + R + 1) * C;
+    wlo = wlo < 0 ? 0 : wlo;
+    whi = whi > F ? F : whi;
+    if (whi > wlo) {
+      win_lo = (int)(wlo * TPF);
+      win_hi = (int)(whi * TPF);
     }
   }
 
@@ -504,15 +516,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
       vl[e] = smem_a + 4 * TILE + lds_off<RB, false>(4 * lg + (qi >> 2), (16 * e + 4 * (qi & 3)) * 2);
   }
 
-  // One 32-key step (kc) of the tile in stage G.
-  auto step = [&](auto G_, auto KC_, int k0) {
+  // ---- S^T and dS^T of 32-key step KC of the tile in stage G ----
+  // sacc[kb2][i] is the score of key kb + 16 kb2 + 4 lg + i for query qi
+  auto scores = [&](auto G_, auto KC_, f32x4 (&sacc)[2], f32x4 (&dsacc)[2]) __attribute__((always_inline)) {
     constexpr int G = decltype(G_)::value;
-    constexpr int KC = decltype(KC_)::value;
-    constexpr int kb = KC * CK;                     // first key of the step in the tile
-
-    // ---- S^T and dS^T for the two 16-key blocks of the step ----
-    // sacc[kb2][i] is the score of key kb + 16 kb2 + 4 lg + i for query qi
-    f32x4 sacc[2], dsacc[2];
+    constexpr int kb = decltype(KC_)::value * CK;
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
       f32x4 s_ = f32x4{}, ds_ = f32x4{};
@@ -528,44 +536,32 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
       sacc[kb2] = s_;
       dsacc[kb2] = ds_;
     }
+  };
 
-    // ---- masks: key tail and partial frame-window tiles ----
-    const int ka = k0 + kb;                // first key of the step
-    const bool tail = ka + CK > N;
-    bool partial = false;
-    if constexpr (MASKED) {
-      const int kz = ka + CK;
-      const bool in_win = ka >= win_lo && kz <= win_hi;
-      const bool in_first = p.mask.first && kz <= p.mask.tpf;
-      const bool in_last = p.mask.last && ka >= (p.mask.frames - 1) * p.mask.tpf;
-      partial = !(in_win || in_first || in_last);
-    }
-    if (tail || partial) {
+  // ---- element masks (key tail, partial frame-window tiles) ----
+  // ka is the first key of the step.  Straight-line selects: the visibility
+  // of every element is computed, with no per-lane branch.
+  auto apply_mask = [&](int ka, f32x4 (&sacc)[2], f32x4 (&dsacc)[2]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = ka + 16 * kb2 + 4 * lg + i;
-          bool vis = key < N;
-          if constexpr (MASKED) {
-            if (partial && vis && !q_all) {
-              const int kf_ = div_fix(key, p.mask.tpf, p.mask.inv_tpf);
-              const int kc_ = div_fix(kf_, p.mask.chunk, p.mask.inv_chunk);
-              const int dc = kc_ > q_chunk ? kc_ - q_chunk : q_chunk - kc_;
-              vis = dc <= p.mask.radius || (p.mask.first && kf_ == 0) ||
-                    (p.mask.last && kf_ == p.mask.frames - 1);
-            }
-          }
-          if (!vis) {
-            sacc[kb2][i] = -INFINITY;
-            dsacc[kb2][i] = 0.f;
-          }
+      for (int i = 0; i < 4; ++i) {
+        const int key = ka + 16 * kb2 + 4 * lg + i;
+        bool vis = key < N;
+        if constexpr (MASKED) {
+          // bitwise, not short-circuit: no branch per element
+          const bool in_chunks = (unsigned)(key - kv_lo) < (unsigned)(kv_hi - kv_lo);
+          vis = vis & (in_chunks | (key < a_first_hi) | (key >= a_last_lo));
         }
+        sacc[kb2][i] = vis ? sacc[kb2][i] : -INFINITY;
+        dsacc[kb2][i] = vis ? dsacc[kb2][i] : 0.f;
       }
     }
+  };
 
-    // ---- online softmax (log2 domain, lazy rescale) ----
-    // IEEE maximum (NaN-propagating): v_maximum3_f32, no canonicalisation
+  // ---- running max (log2 domain) and lazy rescale of the accumulators ----
+  // IEEE maximum (NaN-propagating): v_maximum3_f32, no canonicalisation
+  auto update_max = [&](const f32x4 (&sacc)[2]) __attribute__((always_inline)) {
     const f32x4 m2 = __builtin_elementwise_maximum(sacc[0], sacc[1]);
     float mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m2[0], m2[1]),
                                              __builtin_elementwise_maximum(m2[2], m2[3]));
@@ -583,6 +579,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
       }
       m_run = m_new;
     }
+  };
+
+  // ---- P~ = exp2(S - m) and H = P~ . dS (in place), row sums l and r ----
+  auto softmax = [&](f32x4 (&sacc)[2], f32x4 (&dsacc)[2]) __attribute__((always_inline)) {
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -596,8 +596,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
         dsacc[kb2][i] = hv;
       }
     }
+  };
 
-    // ---- O^T += V^T P^T ; T^T += dV^T P^T + V^T H^T ----
+  // ---- O^T += V^T P^T ; T^T += dV^T P^T + V^T H^T for step KC of stage G ----
+  auto accumulate = [&](auto G_, auto KC_, const f32x4 (&sacc)[2], const f32x4 (&dsacc)[2]) __attribute__((always_inline)) {
+    constexpr int G = decltype(G_)::value;
+    constexpr int kb = decltype(KC_)::value * CK;
     if constexpr (BF16) {
       // B operand: lane (query qi, group lg) gives keys 4lg + 0..3 and
       // 16 + 4lg + 0..3 of the step, in that order
@@ -613,7 +617,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
       // keys of V and dV -- four transpose reads.  Groups e+1 and e+2 are in
       // flight while group e feeds its MFMAs.
       constexpr int VO = G * TILE + kb * RB;          // stage and step rows
-      auto issue = [&](auto e_, i16x4 (&r)[4]) {
+      auto issue = [&](auto e_, i16x4 (&r)[4]) __attribute__((always_inline)) {
         constexpr int e = decltype(e_)::value;
         r[0] = lds_read_tr<VO>(vl[e]);
         r[1] = lds_read_tr<VO + 16 * RB>(vl[e]);
@@ -623,7 +627,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
       i16x4 buf[3][4];
       issue(std::integral_constant<int, 0>{}, buf[0]);
       if constexpr (ND > 1) issue(std::integral_constant<int, 1>{}, buf[1]);
-      static_for<0, ND>([&](auto e_) {
+      static_for<0, ND>([&](auto e_) __attribute__((always_inline)) {
         constexpr int e = decltype(e_)::value;
         i16x4(&cur)[4] = buf[e % 3];
         if constexpr (e + 2 < ND) {
@@ -661,15 +665,59 @@ __global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
     }
   };
 
-  // One tile in stage G: wait for it, release the other stage to the copy of
-  // the next tile, then its 32-key steps.
-  auto tile = [&](auto G_, int it) {
-    constexpr int G = decltype(G_)::value;
+  // Does the tile at key k0 need element masks?  Only the key tail, and in
+  // the frame-window case a tile not wholly inside the block's common window
+  // or an anchor frame.
+  auto needs_mask = [&](int k0) __attribute__((always_inline)) {
+    const int kz = k0 + BN;
+    bool m = kz > N;
+    if constexpr (MASKED) {
+      const bool in_win = k0 >= win_lo && kz <= win_hi;
+      const bool in_first = p.mask.first && kz <= p.mask.tpf;
+      const bool in_last = p.mask.last && k0 >= (p.mask.frames - 1) * p.mask.tpf;
+      m = m || !(in_win || in_first || in_last);
+    }
+    return m;
+  };
+
+  // One tile of two 32-key steps a, b in stage G: wait for it, release the
+  // other stage to the copy of the next tile, then the steps.  At d = 128 the
+  // order puts independent work side by side: the scores of b next to the
+  // exponentials of a, the products of a next to the running max of b.  At
+  // d = 64 (half the MFMAs per step) the plain order measures faster.  The
+  // element masks sit behind a branch that is uniform over the tile, placed
+  // where the order already ends a block.
+  static_assert(BN == 2 * CK, "two steps per tile");
+  constexpr bool kOverlap = BF16 && D >= 128;
+  auto tile = [&](auto G_, int it) __attribute__((always_inline)) {
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
     const int k0 = tile_at(tr, it) * BN;
+    const bool need = needs_mask(k0);
     wait_vmem();
     __syncthreads();   // tile `it` landed; every wave is done with tile it-1
-    if (it + 1 < ntile) copier.issue(tile_at(tr, it + 1) * BN, N, smem, 1 - G);
-    static_for<0, BN / CK>([&](auto kc) { step(G_, kc, k0); });
+    if (it + 1 < ntile) copier.issue(tile_at(tr, it + 1) * BN, N, smem, 1 - decltype(G_)::value);
+    f32x4 sa[2], dsa[2], sb[2], dsb[2];
+    scores(G_, C0{}, sa, dsa);
+    if (need) apply_mask(k0, sa, dsa);
+    update_max(sa);
+    if constexpr (kOverlap) {
+      scores(G_, C1{}, sb, dsb);
+      softmax(sa, dsa);
+      // the exponentials of a are computed here, beside the scores of b, not
+      // sunk past the mask branch below
+      asm volatile("" ::"v"(sa[0]), "v"(sa[1]), "v"(dsa[0]), "v"(dsa[1]));
+      if (need) apply_mask(k0 + CK, sb, dsb);
+      accumulate(G_, C0{}, sa, dsa);
+    } else {
+      softmax(sa, dsa);
+      accumulate(G_, C0{}, sa, dsa);
+      scores(G_, C1{}, sb, dsb);
+      if (need) apply_mask(k0 + CK, sb, dsb);
+    }
+    update_max(sb);
+    softmax(sb, dsb);
+    accumulate(G_, C1{}, sb, dsb);
   };
 
   int it = 0;
