@@ -15,10 +15,11 @@ import ctypes
 import os
 
 __all__ = [
-    "ATTN_JVP_BF16", "ATTN_JVP_FP32", "AttnJvpError", "Layout", "Mask",
-    "attn_jvp_check", "attn_jvp_fwd", "attn_jvp_fwd_strided",
-    "attn_jvp_status_string", "attn_jvp_tile_shape", "attn_jvp_visible_tiles",
-    "exported_symbols", "fwd", "library_path", "load",
+    "ATTN_JVP_BF16", "ATTN_JVP_FP32", "AttnJvpError", "Layout", "Mask", "Shape",
+    "attn_jvp_check", "attn_jvp_check_ex", "attn_jvp_fwd", "attn_jvp_fwd_ex",
+    "attn_jvp_fwd_strided", "attn_jvp_status_string", "attn_jvp_tile_shape",
+    "attn_jvp_tile_shape_ex", "attn_jvp_visible_tiles", "exported_symbols", "fwd",
+    "library_path", "load",
 ]
 
 ATTN_JVP_BF16 = 0
@@ -52,10 +53,16 @@ class Layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64 * 3) for n in ("q", "k", "v", "dq", "dk", "dv", "o", "dout")]
 
 
+class Shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "heads", "seqlen_q", "seqlen_kv", "head_dim_qk", "head_dim_v")]
+
+
 _lib = None
 
-EXPORTS = ("attn_jvp_fwd", "attn_jvp_fwd_strided", "attn_jvp_check",
-           "attn_jvp_tile_shape", "attn_jvp_visible_tiles", "attn_jvp_status_string")
+EXPORTS = ("attn_jvp_fwd", "attn_jvp_fwd_strided", "attn_jvp_fwd_ex", "attn_jvp_check",
+           "attn_jvp_check_ex", "attn_jvp_tile_shape", "attn_jvp_tile_shape_ex",
+           "attn_jvp_visible_tiles", "attn_jvp_status_string")
 
 
 def library_path():
@@ -81,6 +88,14 @@ def load():
     lib.attn_jvp_check.argtypes = ptrs10 + [i32, i32, i32, i32, i32,
                                             ctypes.POINTER(Layout), ctypes.POINTER(Mask)]
     lib.attn_jvp_check.restype = i32
+    lib.attn_jvp_fwd_ex.argtypes = ptrs10 + [ctypes.POINTER(Shape), f32, i32,
+                                             ctypes.POINTER(Layout), ctypes.POINTER(Mask), vp]
+    lib.attn_jvp_fwd_ex.restype = i32
+    lib.attn_jvp_check_ex.argtypes = ptrs10 + [ctypes.POINTER(Shape), i32,
+                                               ctypes.POINTER(Layout), ctypes.POINTER(Mask)]
+    lib.attn_jvp_check_ex.restype = i32
+    lib.attn_jvp_tile_shape_ex.argtypes = [i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.attn_jvp_tile_shape_ex.restype = i32
     lib.attn_jvp_tile_shape.argtypes = [i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.attn_jvp_tile_shape.restype = i32
     lib.attn_jvp_visible_tiles.argtypes = [i32, i32, i32, ctypes.POINTER(Mask), i64p]
@@ -127,6 +142,28 @@ def attn_jvp_check(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, B, H, N, d, dtype, lay
                                  dtype, lay, _mask_ptr(mask))
 
 
+def attn_jvp_fwd_ex(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, shape, scale, dtype,
+                    layout=None, mask=None, stream=None):
+    lay = None if layout is None else ctypes.byref(layout)
+    return load().attn_jvp_fwd_ex(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, ctypes.byref(shape),
+                                  scale, dtype, lay, _mask_ptr(mask), stream)
+
+
+def attn_jvp_check_ex(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, shape, dtype, layout=None,
+                      mask=None):
+    lay = None if layout is None else ctypes.byref(layout)
+    return load().attn_jvp_check_ex(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE,
+                                    ctypes.byref(shape), dtype, lay, _mask_ptr(mask))
+
+
+def attn_jvp_tile_shape_ex(dtype, d_qk, d_v):
+    bm, bn = ctypes.c_int(), ctypes.c_int()
+    st = load().attn_jvp_tile_shape_ex(dtype, d_qk, d_v, ctypes.byref(bm), ctypes.byref(bn))
+    if st != 0:
+        raise AttnJvpError(st, "attn_jvp_tile_shape_ex")
+    return bm.value, bn.value
+
+
 def attn_jvp_tile_shape(dtype, d):
     bm, bn = ctypes.c_int(), ctypes.c_int()
     st = load().attn_jvp_tile_shape(dtype, d, ctypes.byref(bm), ctypes.byref(bn))
@@ -166,34 +203,45 @@ def layout_of(q, k, v, dq, dk, dv, o, do):
 
 
 def fwd(q, k, v, dq, dk, dv, scale=None, mask=None, out=None):
-    """(o, do, lse, dlse) for [B, H, N, d] CUDA tensors (bf16 or float32).
+    """(o, do, lse, dlse) for CUDA tensors q [B, H, Lq, d_qk], k [B, H, Lkv,
+    d_qk], v [B, H, Lkv, d_v] (bf16 or float32).
 
     Tangents must have their primal's shape and strides.  ``mask`` is None or
-    a frame-window dict/Mask.  Outputs are allocated contiguous unless
+    a frame-window dict/Mask (self-attention, Lq == Lkv).  Outputs o, do
+    [B, H, Lq, d_v] and lse, dlse [B, H, Lq] are allocated contiguous unless
     ``out = (o, do, lse, dlse)`` is given.  Runs on the current stream.
     """
     import torch
     dtypes = {torch.bfloat16: ATTN_JVP_BF16, torch.float32: ATTN_JVP_FP32}
     if q.dtype not in dtypes:
         raise TypeError(f"unsupported dtype {q.dtype}")
-    B, H, N, d = q.shape
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-d [B, H, L, d]")
+    B, H, Lq, dqk = q.shape
+    Lkv, dv_ = k.shape[2], v.shape[3]
+    if tuple(k.shape) != (B, H, Lkv, dqk) or tuple(v.shape) != (B, H, Lkv, dv_):
+        raise ValueError("shapes must be q [B,H,Lq,d_qk], k [B,H,Lkv,d_qk], v [B,H,Lkv,d_v]")
+    for t, ref in ((dq, q), (dk, k), (dv, v)):
+        if t.shape != ref.shape:
+            raise ValueError("each tangent must have its primal's shape")
+    for t in (k, v, dq, dk, dv):
+        if t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v, dq, dk, dv must share dtype and device")
     if out is None:
-        o = torch.empty((B, H, N, d), device=q.device, dtype=q.dtype)
+        o = torch.empty((B, H, Lq, dv_), device=q.device, dtype=q.dtype)
         do = torch.empty_like(o)
-        lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
+        lse = torch.empty((B, H, Lq), device=q.device, dtype=torch.float32)
         dlse = torch.empty_like(lse)
     else:
         o, do, lse, dlse = out
-    for t in (k, v, dq, dk, dv):
-        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
-            raise ValueError("q, k, v, dq, dk, dv must share shape, dtype and device")
     lay = layout_of(q, k, v, dq, dk, dv, o, do)
+    shape = Shape(B, H, Lq, Lkv, dqk, dv_)
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = attn_jvp_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), dq.data_ptr(),
-                              dk.data_ptr(), dv.data_ptr(), o.data_ptr(), do.data_ptr(),
-                              lse.data_ptr(), dlse.data_ptr(), B, H, N, d,
-                              0.0 if scale is None else float(scale), dtypes[q.dtype],
-                              lay, mask, stream)
+    st = attn_jvp_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), dq.data_ptr(),
+                         dk.data_ptr(), dv.data_ptr(), o.data_ptr(), do.data_ptr(),
+                         lse.data_ptr(), dlse.data_ptr(), shape,
+                         0.0 if scale is None else float(scale), dtypes[q.dtype],
+                         lay, mask, stream)
     if st != 0:
-        raise AttnJvpError(st, "attn_jvp_fwd_strided")
+        raise AttnJvpError(st, "attn_jvp_fwd_ex")
     return o, do, lse, dlse

@@ -1,39 +1,9 @@
-// Fused attention forward-mode derivative (JVP) for AMD gfx950 (MI355X).
-//
-// What is computed (page "带分数正则的一致性蒸馏", gitcode.csdn.net, section
-// 注意力): per query row, O = softmax(s Q K^T) V together with its tangent
-// dO = P dV + (P (.) dS) V - rowsum(P (.) dS) O, dS = s (dQ K^T + Q dK^T), the
-// natural-log row log-sum-exp and its tangent.  The pages stream K/V blocks
-// with an online max m, sum l, tangent sum r and accumulators O~, A~ = P~ dV,
-// B~ = H~ V (H~ = P~ (.) dS); only A~ + B~ is ever used, so this kernel keeps
-// a single tangent accumulator T~ = A~ + B~.
-//
-// gfx950 design (one workgroup = 4 waves = 128 query rows of one (b, h)):
-//   * every wave owns 32 query rows and computes the TRANSPOSED score tile
-//     S^T = K Q^T with v_mfma_f32_32x32x16_bf16: each lane then holds all of
-//     its query's scores for 16 of the 32 keys, so the row max needs one
-//     cross-lane step, the row sums stay lane-local until the epilogue, and
-//     the score fragment is already the B operand of the value products;
-//   * Q and dQ stay in registers (B operands) for the whole key loop;
-//   * K, dK, V, dV tiles move global -> LDS with asynchronous
-//     global_load_lds_dwordx4 copies into two LDS stages (the next tile
-//     streams in while the current one is consumed; no register staging),
-//     row-major with an XOR swizzle of the 16-byte chunks;
-//   * the value products need V and dV transposed (keys along the MFMA k
-//     dimension): ds_read_b64_tr_b16 transposes 4 keys x 4 columns per
-//     16-lane group on the way out of LDS;
-//   * O^T and T^T (= (A~ + B~)^T) accumulate in 32x32 fp32 fragments: every
-//     value a lane holds belongs to its own query, so the online rescale is
-//     one multiply by a per-lane factor, and it is skipped unless the row
-//     max grew by more than 2^8;
-//   * exp2 domain for the scores (scale * log2 e folded into one FMA), the
-//     tangent stays in natural units;
-//   * workgroup ids are remapped so that all query blocks of one (b, h) land
-//     on the same XCD (dispatch round-robins consecutive ids over the 8 XCDs),
-//     keeping that head's K/V/dK/dV in one L2;
-//   * with a frame-window mask, each query block walks only the key-tile
-//     ranges some of its rows can see; element masks run on partial tiles.
-// float32 inputs use the same structure with v_mfma_f32_32x32x2_f32.
+// Host side of the attn_jvp C ABI: argument checks, launch shapes and
+// dispatch to the kernel instances (kernel.h, instantiated per head dim in
+// the inst_*.hip units).  The op contract (shape rules, tangents sharing the
+// primals' strides, default scale d_qk^-1/2, outputs allocated by the
+// caller, O and dO in the input dtype, LSE in float32) follows the page
+// "带分数正则的一致性蒸馏" (gitcode.csdn.net), section 注意力, 前向 kernel.
 
 #include <hip/hip_runtime.h>
 
@@ -41,732 +11,51 @@
 #include <stdint.h>
 #include <string.h>
 
-#include <type_traits>
-
 #include "attn_jvp.h"
+#include "dispatch.h"
+
+namespace attn_jvp {
+
+namespace {
+template <typename T, int DQK>
+bool shape_dv(int dv, Shape *out) {
+  switch (dv) {
+    case 16: *out = shape_of<T, DQK, 16>(); return true;
+    case 32: *out = shape_of<T, DQK, 32>(); return true;
+    case 64: *out = shape_of<T, DQK, 64>(); return true;
+    case 128: if (sizeof(T) == 2) { *out = shape_of<T, DQK, 128>(); return true; } return false;
+    case 256: if (sizeof(T) == 2) { *out = shape_of<T, DQK, 256>(); return true; } return false;
+    default: return false;
+  }
+}
+}  // namespace
+
+bool shape_for(bool bf16, int dqk, int dv, Shape *out) {
+  if (bf16) {
+    switch (dqk) {
+      case 16: return shape_dv<__bf16, 16>(dv, out);
+      case 32: return shape_dv<__bf16, 32>(dv, out);
+      case 64: return shape_dv<__bf16, 64>(dv, out);
+      case 128: return shape_dv<__bf16, 128>(dv, out);
+      case 256: return shape_dv<__bf16, 256>(dv, out);
+      default: return false;
+    }
+  }
+  switch (dqk) {
+    case 16: return shape_dv<float, 16>(dv, out);
+    case 32: return shape_dv<float, 32>(dv, out);
+    case 64: return shape_dv<float, 64>(dv, out);
+    default: return false;
+  }
+}
+
+}  // namespace attn_jvp
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kWaves = 8;                      // two waves per SIMD
-constexpr int kThreads = 64 * kWaves;
-constexpr int kWaveRows = 16;                  // query rows per wave
-constexpr int kBlockM = kWaves * kWaveRows;    // query rows per workgroup
-
-// ---------------------------------------------------------------------------
-// Element traits: operand fragment per lane for the 16x16 MFMA family.  For
-// an operand tile with 16 rows (or columns) and K along the contraction, lane
-// l holds row l % 16 and the K slice of lane group l / 16; the 16x16 result
-// puts column l % 16 and rows 4 (l / 16) + 0..3 in lane l.
-// ---------------------------------------------------------------------------
-template <typename T> struct Elem;
-
-template <> struct Elem<__bf16> {
-  using Frag = bf16x8;            // 8 bf16 along K per lane
-  static constexpr int KL = 8;    // K elements per lane
-  static constexpr int KI = 32;   // K per instruction (four lane groups)
-  __device__ static inline f32x4 mfma(Frag a, Frag b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  }
-};
-
-template <> struct Elem<float> {
-  using Frag = float;
-  static constexpr int KL = 1;
-  static constexpr int KI = 4;
-  __device__ static inline f32x4 mfma(Frag a, Frag b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-  }
-};
-
-// ---------------------------------------------------------------------------
-// Frame-window mask (page "VDN-Minimax-H3 ... Stage A1", yfxerp.com).
-// ---------------------------------------------------------------------------
-struct MaskDev {
-  int kind;        // 0 none, 1 frame window
-  int frames, tpf, chunk, radius;
-  int first, last, see_all;
-  float inv_tpf, inv_chunk;
-};
-
-// floor(n / den) for 0 <= n < 2^24 from a float estimate and exact fix-up.
-__host__ __device__ inline int div_fix(int n, int den, float inv) {
-  int q = (int)((float)n * inv);
-  q -= (q * den > n);
-  q -= (q * den > n);
-  q += ((q + 1) * den <= n);
-  q += ((q + 1) * den <= n);
-  return q;
-}
-
-struct TileRanges {
-  int n;
-  int lo[3], hi[3];   // key-tile index ranges [lo, hi), ascending, disjoint
-};
-
-// Key-tile ranges that some query of rows [q_lo, q_hi) can see.
-__host__ __device__ inline TileRanges visible_tiles(const MaskDev &m, int q_lo,
-                                                    int q_hi, int N, int BN) {
-  TileRanges tr;
-  const int ntiles = (N + BN - 1) / BN;
-  tr.n = 1;
-  tr.lo[0] = 0;
-  tr.hi[0] = ntiles;
-  tr.lo[1] = tr.hi[1] = tr.lo[2] = tr.hi[2] = 0;
-  if (m.kind == 0) return tr;
-  const int T = m.tpf, C = m.chunk, F = m.frames, R = m.radius;
-  const int qf0 = q_lo / T, qf1 = (q_hi - 1) / T;
-  if (m.see_all && ((m.first && qf0 == 0) || (m.last && qf1 == F - 1))) return tr;
-  const int c0 = qf0 / C, c1 = qf1 / C;
-  int f_lo = (c0 - R) * C;
-  if (f_lo < 0) f_lo = 0;
-  long long f_hi_l = (long long)(c1 + R + 1) * C;
-  int f_hi = f_hi_l > F ? F : (int)f_hi_l;
-  // candidate key-tile intervals in ascending order of start: first-frame
-  // anchor, chunk window, last-frame anchor; merged where they touch
-  // (static indices only, so nothing is spilled to memory)
-  tr.n = 0;
-  tr.lo[0] = tr.hi[0] = tr.lo[1] = tr.hi[1] = tr.lo[2] = tr.hi[2] = 0;
-  const bool valid[3] = {m.first != 0, true, m.last != 0};
-  const int a_[3] = {0, f_lo * T / BN, (F - 1) * T / BN};
-  const int z_[3] = {(T + BN - 1) / BN, (f_hi * T + BN - 1) / BN, (F * T + BN - 1) / BN};
-#pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    if (!valid[i]) continue;
-    const int a = a_[i], z = z_[i];
-    if (tr.n == 0) {
-      tr.lo[0] = a; tr.hi[0] = z; tr.n = 1;
-    } else if (tr.n == 1) {
-      if (a <= tr.hi[0]) tr.hi[0] = z > tr.hi[0] ? z : tr.hi[0];
-      else { tr.lo[1] = a; tr.hi[1] = z; tr.n = 2; }
-    } else {
-      if (a <= tr.hi[1]) tr.hi[1] = z > tr.hi[1] ? z : tr.hi[1];
-      else { tr.lo[2] = a; tr.hi[2] = z; tr.n = 3; }
-    }
-  }
-  return tr;
-}
-
-// ---------------------------------------------------------------------------
-// Kernel parameters.
-// ---------------------------------------------------------------------------
-struct Params {
-  const void *q, *k, *v, *dq, *dk, *dv;
-  void *o, *dout;
-  float *lse, *dlse;
-  int64_t sq[3], sk[3], sv[3], so[3];   // (b, h, n) element strides
-  int B, H, N;
-  int nqb;                              // query blocks per (b, h)
-  float scale, scale_log2;
-  MaskDev mask;
-};
-
-__device__ inline int logical_block_id() {
-  // Dispatch places workgroup w on XCD (w mod 8).  Give each XCD a
-  // contiguous run of logical ids so a head's query blocks share one L2.
-  const int w = blockIdx.x, n = gridDim.x;
-  const int per = n / 8, rem = n % 8;
-  const int x = w % 8, local = w / 8;
-  return x * per + (x < rem ? x : rem) + local;
-}
-
-// ---------------------------------------------------------------------------
-// LDS tile layout.  A K, dK, V or dV tile is BN rows of RB = d * sizeof(T)
-// bytes, row-major (one key per row).  The 16-byte chunks of row r are XOR
-// permuted, with one rule for the tiles read as MFMA operand rows (K, dK) and
-// another for the tiles read by transposing loads (V, dV):
-//  * K side, kswz(r): the sweep index r / (256 / RB) of the row, mod the
-//    chunks per row.  16 consecutive rows read at one logical chunk then fill
-//    every 16-byte slot of a 256-byte bank sweep once, and the rows two
-//    lane groups read at neighbouring chunks stay apart as well.
-//  * V side, vswz(r): 8 consecutive rows, each read as a 32-byte run by four
-//    lanes of a transpose load, touch every bank once.
-// Both rules repeat every 16 rows, so a row offset that is a multiple of 16
-// keeps a lane's swizzle.
-// ---------------------------------------------------------------------------
-template <int RB>
-__device__ inline int kswz(int r) {
-  constexpr int CPR = RB / 16;            // chunks per row
-  constexpr int RPB = 256 / RB;           // rows per 256-byte bank sweep
-  return (r / RPB) % CPR;
-}
-
-template <int RB>
-__device__ inline int vswz(int r) {
-  constexpr int CPR = RB / 16;
-  constexpr int RPB = 256 / RB;
-  constexpr int H = CPR / 2;
-  const int m = r / RPB;
-  return ((m % H) << 1) | ((m / H) % 2);
-}
-
-template <int RB, bool KSIDE>
-__device__ inline int lds_off(int r, int byte_col) {
-  const int x = KSIDE ? kswz<RB>(r) : vswz<RB>(r);
-  return r * RB + ((((byte_col >> 4) ^ x)) << 4) + (byte_col & 15);
-}
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Read 4 consecutive-key bf16 values of one d column: ds_read_b64_tr_b16.
-// In each 16-lane group, lane i receives element (i % 4) of the 8-byte chunks
-// addressed by lanes i/4, i/4 + 4, i/4 + 8 and i/4 + 12 (in that order).
-//
-// Issued through inline asm: the compiler cannot tell that these reads never
-// touch the LDS stage an in-flight global->LDS copy is filling, and would
-// otherwise wait for every outstanding copy (vmcnt(0)) before the first one,
-// serialising the tile prefetch.  The compiler does not count these reads, so
-// lds_tr_wait() must run before their results are used; extra LDS operations
-// it does not know about only make its own lgkmcnt waits stronger, since LDS
-// operations complete in issue order.
-template <int OFF>
-__device__ inline i16x4 lds_read_tr(uint32_t addr) {
-  static_assert(OFF >= 0 && OFF < 65536, "DS offset field");
-  i16x4 v;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
-  return v;
-}
-
-__device__ inline uint32_t lds_addr(const void *p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
-}
-
-// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
-template <int B, int E, typename F>
-__device__ __attribute__((always_inline)) inline void static_for(F &&f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
-  }
-}
-
-// Wait until at most N LDS operations are outstanding; the four values pass
-// through the asm so that nothing reading them can be scheduled before it.
-template <int N>
-__device__ inline void lds_tr_wait(i16x4 &a, i16x4 &b, i16x4 &c, i16x4 &d) {
-  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "n"(N));
-}
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// 16-byte LDS read of a K or dK operand, issued through inline asm for the
-// same reason as the transpose reads (and so that the reads of the next
-// k-step can be put in flight ahead of the current k-step's MFMAs).
-__device__ inline i32x4 lds_read_b128(const char *p) {
-  const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
-  i32x4 v;
-  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(a));
-  return v;
-}
-
-template <int N>
-__device__ inline void lds_wait(i32x4 &a, i32x4 &b, i32x4 &c, i32x4 &d) {
-  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "n"(N));
-}
-
-// Sum and maximum over the four lanes l, l^16, l^32, l^48 that hold one
-// query row.  v_permlane16_swap(x, x) returns rows (x0, x0, x2, x2) and
-// (x1, x1, x3, x3) of x's four 16-lane rows, and v_permlane32_swap(x, x)
-// returns halves (lo, lo) and (hi, hi): combining the pair is one butterfly
-// step, done in the VALU without an LDS round trip.  Every lane of the row
-// ends with the same bits (same operand order on both sides).
-__device__ inline float row_sum4(float x) {
-  const unsigned u = __float_as_uint(x);
-  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const unsigned v = __float_as_uint(x);
-  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-__device__ inline float row_max4(float x) {
-  const unsigned u = __float_as_uint(x);
-  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  x = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const unsigned v = __float_as_uint(x);
-  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
-// Asynchronous global->LDS copies of key tiles (K, dK, V, dV).  Each wave
-// instruction fills 1 KiB of LDS contiguously, lane l writing bytes
-// [16 l, 16 l + 16); the lane picks the global chunk that the swizzled layout
-// puts there.  The per-lane byte offsets inside a tile are fixed, so they are
-// computed once; a tile then only moves the (scalar) base pointers.  Rows
-// past the end of the sequence re-read row N-1 (their scores are masked to
-// -inf and their tangents to 0).
-template <typename T, int D, int BN>
-struct TileCopier {
-  static constexpr int RB = D * (int)sizeof(T);
-  static constexpr int CPR = RB / 16;
-  static constexpr int TILE = BN * RB;
-  static constexpr int IPW = TILE / 1024 / kWaves;   // wave instructions per tensor
-  static_assert(IPW * 1024 * kWaves == TILE, "tile must split over the waves");
-
-  const char *base[4];      // byte base of K, dK, V, dV for this (b, h)
-  int64_t rstride[4];       // row stride in bytes
-  uint32_t rs_k, rs_v;      // the same, 32-bit (below 2^24, checked on the host)
-  uint32_t slot[IPW];       // (row << 16) | (K-side chunk * 16) << 8 | V-side chunk * 16
-  int wave;                 // wave index (uniform)
-
-  __device__ void init(const T *const src[4], const int64_t stride[4], int wave_, int lane) {
-    wave = wave_;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      base[t] = (const char *)src[t];
-      rstride[t] = stride[t] * (int64_t)sizeof(T);
-    }
-    rs_k = (uint32_t)rstride[0];
-    rs_v = (uint32_t)rstride[2];
-#pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-      const int s = (wave * IPW + i) * 64 + lane;
-      const int r = s / CPR;
-      const int ck = (s % CPR) ^ kswz<RB>(r);
-      const int cv = (s % CPR) ^ vswz<RB>(r);
-      slot[i] = ((uint32_t)r << 16) | (uint32_t)(ck * 16) << 8 | (uint32_t)(cv * 16);
-    }
-  }
-
-  // LDS layout: tensor t, stage g at smem + (2 t + g) TILE
-  __device__ void issue(int k0, int N, char *smem, int g) const {
-    const int valid = (N - k0 < BN ? N - k0 : BN) - 1;   // last real row
-    const char *tb[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) tb[t] = base[t] + (int64_t)k0 * rstride[t];
-#pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-      uint32_t r = slot[i] >> 16;
-      r = r < (uint32_t)valid ? r : (uint32_t)valid;
-      const uint32_t ok = __umul24(r, rs_k) + ((slot[i] >> 8) & 0xffu);
-      const uint32_t ov = __umul24(r, rs_v) + (slot[i] & 0xffu);
-      char *dst = smem + g * TILE + (wave * IPW + i) * 1024;
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        __builtin_amdgcn_global_load_lds((const void *)(tb[t] + (t < 2 ? ok : ov)),
-                                         (lds_void *)(dst + 2 * t * TILE), 16, 0, 0);
-    }
-  }
-};
-
-__device__ inline void wait_vmem() {
-  // s_waitcnt vmcnt(0): every global->LDS copy this wave issued has landed
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-}
-
-// Tile index of the idx-th visited tile.
-__device__ inline int tile_at(const TileRanges &tr, int idx) {
-  int t = tr.lo[0] + idx;
-  if (tr.n > 1 && t >= tr.hi[0]) {
-    t = tr.lo[1] + (t - tr.hi[0]);
-    if (tr.n > 2 && t >= tr.hi[1]) t = tr.lo[2] + (t - tr.hi[1]);
-  }
-  return t;
-}
-
-// Lazy rescale: the running max only moves when a tile's max exceeds it by
-// more than 2^8 (P~ then stays below 256); the final normalisation uses the
-// same reference, so the result is unchanged.
-constexpr float kRescaleThreshold = 8.0f;
-
-template <typename T, int D, int BN, int CK, bool MASKED>
-__global__ __launch_bounds__(kThreads, 1) void attn_jvp_kernel(Params p) {
-  using E = Elem<T>;
-  using Frag = typename E::Frag;
-  constexpr bool BF16 = sizeof(T) == 2;
-  constexpr int KL = E::KL;
-  constexpr int KI = E::KI;
-  constexpr int RB = D * (int)sizeof(T);      // bytes per LDS row
-  constexpr int TILE = BN * RB;               // bytes per tensor tile
-  constexpr int STAGE = 4 * TILE;             // K, dK, V, dV
-  constexpr int DS = D / KI;                  // k-steps over d
-  constexpr int ND = D / 16;                  // 16-wide d blocks
-  static_assert(CK == 32 && BN % CK == 0 && D % 32 == 0, "tile shape");
-
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
-  const int qi = lane & 15;        // this lane's query within the wave
-  const int lg = lane >> 4;        // lane group 0..3
-
-  const int lid = logical_block_id();
-  const int bh = lid / p.nqb;
-  const int qb = lid - bh * p.nqb;
-  const int b = bh / p.H;
-  const int h = bh - b * p.H;
-  const int N = p.N;
-
-  const T *Q = (const T *)p.q + b * p.sq[0] + h * p.sq[1];
-  const T *dQ = (const T *)p.dq + b * p.sq[0] + h * p.sq[1];
-  const T *src[4] = {(const T *)p.k + b * p.sk[0] + h * p.sk[1],
-                     (const T *)p.dk + b * p.sk[0] + h * p.sk[1],
-                     (const T *)p.v + b * p.sv[0] + h * p.sv[1],
-                     (const T *)p.dv + b * p.sv[0] + h * p.sv[1]};
-  const int64_t stride[4] = {p.sk[2], p.sk[2], p.sv[2], p.sv[2]};
-
-  const int q0 = qb * kBlockM;
-  const int q_hi = (q0 + kBlockM < N) ? q0 + kBlockM : N;
-
-  TileRanges tr;
-  if constexpr (MASKED) {
-    tr = visible_tiles(p.mask, q0, q_hi, N, BN);
-  } else {
-    tr.n = 1;
-    tr.lo[0] = 0;
-    tr.hi[0] = (N + BN - 1) / BN;
-    tr.lo[1] = tr.hi[1] = tr.lo[2] = tr.hi[2] = 0;
-  }
-  // unused ranges are empty (lo = hi = 0)
-  const int ntile = (tr.hi[0] - tr.lo[0]) + (tr.hi[1] - tr.lo[1]) + (tr.hi[2] - tr.lo[2]);
-
-  // first tile in flight before anything else
-  TileCopier<T, D, BN> copier;
-  copier.init(src, stride, wave, lane);
-  copier.issue(tile_at(tr, 0) * BN, N, smem, 0);
-
-  const int qrow = q0 + wave * kWaveRows + qi;
-  const bool qvalid = qrow < N;
-
-  // ---- Q, dQ fragments (B operands of S^T = K Q^T), resident ----
-  Frag qf[DS], dqf[DS];
-#pragma unroll
-  for (int s = 0; s < DS; ++s) {
-    if (qvalid) {
-      const int64_t off = (int64_t)qrow * p.sq[2] + s * KI + lg * KL;
-      qf[s] = *(const Frag *)(Q + off);
-      dqf[s] = *(const Frag *)(dQ + off);
-    } else {
-      qf[s] = Frag{};
-      dqf[s] = Frag{};
-    }
-  }
-
-  // O^T and T^T blocks: lane holds d = 16e + 4 lg + 0..3 of query qi
-  // O^T, A^T = (P~ dV)^T and B^T = ((P~ . dS) V)^T blocks (dS without the
-  // scale, applied once in the epilogue): lane holds d = 16e + 4 lg + 0..3 of
-  // query qi.  The row sums l (of P~) and r (of P~ . dS) are taken in fp32
-  // before the bf16 rounding, lane-partial until the epilogue.
-  f32x4 oacc[ND], aacc[ND], bacc[ND];
-#pragma unroll
-  for (int e = 0; e < ND; ++e) {
-    oacc[e] = f32x4{};
-    aacc[e] = f32x4{};
-    bacc[e] = f32x4{};
-  }
-  float l_run = 0.f, r_run = 0.f;
-  float m_run = -INFINITY;   // reference max, log2 units
-
-  const float scale = p.scale;
-  const float c2 = p.scale_log2;
-
-  // Query-side mask terms.  Chunks are runs of whole frames, so the keys
-  // this lane's query sees by the chunk rule form one interval
-  // [kv_lo, kv_hi); the anchor frames add [0, a_first_hi) and
-  // [a_last_lo, N).  Keys in [win_lo, win_hi) and the anchor frames are
-  // visible to every row of the block, so tiles inside them need no mask.
-  int kv_lo = 0, kv_hi = N, a_first_hi = 0, a_last_lo = N;
-  int win_lo = 0, win_hi = 0;
-  if constexpr (MASKED) {
-    const long long F = p.mask.frames, TPF = p.mask.tpf, C = p.mask.chunk, R = p.mask.radius;
-    const int qf_ = div_fix(qvalid ? qrow : 0, p.mask.tpf, p.mask.inv_tpf);
-    const int q_chunk = div_fix(qf_, p.mask.chunk, p.mask.inv_chunk);
-    const bool q_all = p.mask.see_all &&
-                       ((p.mask.first && qf_ == 0) || (p.mask.last && qf_ == p.mask.frames - 1));
-    long long flo = (q_chunk - R) * C, fhi = (q_chunk + R + 1) * C;
-    flo = flo < 0 ? 0 : flo;
-    fhi = fhi > F ? F : fhi;
-    if (!q_all) {
-      kv_lo = (int)(flo * TPF);
-      kv_hi = fhi > flo ? (int)(fhi * TPF) : kv_lo;
-    }
-    a_first_hi = p.mask.first ? (int)TPF : 0;
-    a_last_lo = p.mask.last ? (int)((F - 1) * TPF) : N;
-    // the rows of the whole block: chunks c0..c1
-    const long long c0 = (q0 / TPF) / C;
-    const long long c1 = ((q_hi - 1) / TPF) / C;
-    long long wlo = (c1 - R) * C, whi = (c0 + R + 1) * C;
-    wlo = wlo < 0 ? 0 : wlo;
-    whi = whi > F ? F : whi;
-    if (whi > wlo) {
-      win_lo = (int)(wlo * TPF);
-      win_hi = (int)(whi * TPF);
-    }
-  }
-
-  // Lane-dependent parts of the LDS addresses, fixed for the whole loop.
-  // Rows kb + 16 kb2 + qi (K operand) and kb + 16 u + 4 lg + qi / 4
-  // (transpose reads of V) have the swizzle of their row mod 16, so adding
-  // the step's row offset and the stage/tensor offset is a constant that goes
-  // into the instructions' offset field.
-  const uint32_t smem_a = lds_addr(smem);
-  uint32_t kl[DS];                          // K operand, k-step s
-#pragma unroll
-  for (int s = 0; s < DS; ++s) kl[s] = smem_a + lds_off<RB, true>(qi, (s * KI + lg * KL) * (int)sizeof(T));
-  uint32_t vl[BF16 ? ND : 1];               // V transpose reads, d block e
-  if constexpr (BF16) {
-#pragma unroll
-    for (int e = 0; e < ND; ++e)
-      vl[e] = smem_a + 4 * TILE + lds_off<RB, false>(4 * lg + (qi >> 2), (16 * e + 4 * (qi & 3)) * 2);
-  }
-
-  // ---- S^T and dS^T of 32-key step KC of the tile in stage G ----
-  // sacc[kb2][i] is the score of key kb + 16 kb2 + 4 lg + i for query qi
-  auto scores = [&](auto G_, auto KC_, f32x4 (&sacc)[2], f32x4 (&dsacc)[2]) __attribute__((always_inline)) {
-    constexpr int G = decltype(G_)::value;
-    constexpr int kb = decltype(KC_)::value * CK;
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      f32x4 s_ = f32x4{}, ds_ = f32x4{};
-#pragma unroll
-      for (int s = 0; s < DS; ++s) {
-        const char *kp = smem + (kl[s] - smem_a) + G * TILE + (kb + 16 * kb2) * RB;
-        const Frag kf = *(const Frag *)kp;
-        const Frag dkf = *(const Frag *)(kp + 2 * TILE);
-        s_ = E::mfma(kf, qf[s], s_);
-        ds_ = E::mfma(kf, dqf[s], ds_);
-        ds_ = E::mfma(dkf, qf[s], ds_);
-      }
-      sacc[kb2] = s_;
-      dsacc[kb2] = ds_;
-    }
-  };
-
-  // ---- element masks (key tail, partial frame-window tiles) ----
-  // ka is the first key of the step.  Straight-line selects: the visibility
-  // of every element is computed, with no per-lane branch.
-  auto apply_mask = [&](int ka, f32x4 (&sacc)[2], f32x4 (&dsacc)[2]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = ka + 16 * kb2 + 4 * lg + i;
-        bool vis = key < N;
-        if constexpr (MASKED) {
-          // bitwise, not short-circuit: no branch per element
-          const bool in_chunks = (unsigned)(key - kv_lo) < (unsigned)(kv_hi - kv_lo);
-          vis = vis & (in_chunks | (key < a_first_hi) | (key >= a_last_lo));
-        }
-        sacc[kb2][i] = vis ? sacc[kb2][i] : -INFINITY;
-        dsacc[kb2][i] = vis ? dsacc[kb2][i] : 0.f;
-      }
-    }
-  };
-
-  // ---- running max (log2 domain) and lazy rescale of the accumulators ----
-  // IEEE maximum (NaN-propagating): v_maximum3_f32, no canonicalisation
-  auto update_max = [&](const f32x4 (&sacc)[2]) __attribute__((always_inline)) {
-    const f32x4 m2 = __builtin_elementwise_maximum(sacc[0], sacc[1]);
-    float mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m2[0], m2[1]),
-                                             __builtin_elementwise_maximum(m2[2], m2[3]));
-    mx = row_max4(mx) * c2;
-    if (__any(mx > m_run + kRescaleThreshold)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-      r_run *= alpha;
-#pragma unroll
-      for (int e = 0; e < ND; ++e) {
-        oacc[e] *= alpha;
-        aacc[e] *= alpha;
-        bacc[e] *= alpha;
-      }
-      m_run = m_new;
-    }
-  };
-
-  // ---- P~ = exp2(S - m) and H = P~ . dS (in place), row sums l and r ----
-  auto softmax = [&](f32x4 (&sacc)[2], f32x4 (&dsacc)[2]) __attribute__((always_inline)) {
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][i], c2, -m_use));
-        const float hv = pv * dsacc[kb2][i];
-        l_run += pv;
-        r_run += hv;
-        sacc[kb2][i] = pv;
-        dsacc[kb2][i] = hv;
-      }
-    }
-  };
-
-  // ---- O^T += V^T P^T ; T^T += dV^T P^T + V^T H^T for step KC of stage G ----
-  auto accumulate = [&](auto G_, auto KC_, const f32x4 (&sacc)[2], const f32x4 (&dsacc)[2]) __attribute__((always_inline)) {
-    constexpr int G = decltype(G_)::value;
-    constexpr int kb = decltype(KC_)::value * CK;
-    if constexpr (BF16) {
-      // B operand: lane (query qi, group lg) gives keys 4lg + 0..3 and
-      // 16 + 4lg + 0..3 of the step, in that order
-      bf16x8 pf, hf;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pf[i] = (__bf16)sacc[0][i];
-        pf[4 + i] = (__bf16)sacc[1][i];
-        hf[i] = (__bf16)dsacc[0][i];
-        hf[4 + i] = (__bf16)dsacc[1][i];
-      }
-      // A operand for d block e: lane (d = 16e + qi, group lg) needs the same
-      // keys of V and dV -- four transpose reads.  Groups e+1 and e+2 are in
-      // flight while group e feeds its MFMAs.
-      constexpr int VO = G * TILE + kb * RB;          // stage and step rows
-      auto issue = [&](auto e_, i16x4 (&r)[4]) __attribute__((always_inline)) {
-        constexpr int e = decltype(e_)::value;
-        r[0] = lds_read_tr<VO>(vl[e]);
-        r[1] = lds_read_tr<VO + 16 * RB>(vl[e]);
-        r[2] = lds_read_tr<VO + 2 * TILE>(vl[e]);
-        r[3] = lds_read_tr<VO + 2 * TILE + 16 * RB>(vl[e]);
-      };
-      i16x4 buf[3][4];
-      issue(std::integral_constant<int, 0>{}, buf[0]);
-      if constexpr (ND > 1) issue(std::integral_constant<int, 1>{}, buf[1]);
-      static_for<0, ND>([&](auto e_) __attribute__((always_inline)) {
-        constexpr int e = decltype(e_)::value;
-        i16x4(&cur)[4] = buf[e % 3];
-        if constexpr (e + 2 < ND) {
-          issue(std::integral_constant<int, e + 2>{}, buf[(e + 2) % 3]);
-          lds_tr_wait<8>(cur[0], cur[1], cur[2], cur[3]);
-        } else if constexpr (e + 1 < ND) {
-          lds_tr_wait<4>(cur[0], cur[1], cur[2], cur[3]);
-        } else {
-          lds_tr_wait<0>(cur[0], cur[1], cur[2], cur[3]);
-        }
-        const Frag vf = __builtin_bit_cast(Frag, __builtin_shufflevector(cur[0], cur[1], 0, 1, 2, 3, 4, 5, 6, 7));
-        const Frag dvf = __builtin_bit_cast(Frag, __builtin_shufflevector(cur[2], cur[3], 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[e] = E::mfma(vf, pf, oacc[e]);
-        aacc[e] = E::mfma(dvf, pf, aacc[e]);
-        bacc[e] = E::mfma(vf, hf, bacc[e]);
-      });
-    } else {
-      // float32: k-step (kb2, i) takes key 16 kb2 + 4 lg + i from lane group lg
-      const char *Vs = smem + 4 * TILE + G * TILE;
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kb + 16 * kb2 + 4 * lg + i;
-#pragma unroll
-          for (int e = 0; e < ND; ++e) {
-            const int o = lds_off<RB, false>(key, (16 * e + qi) * 4);
-            const Frag vf = *(const Frag *)(Vs + o);
-            const Frag dvf = *(const Frag *)(Vs + 2 * TILE + o);
-            oacc[e] = E::mfma(vf, sacc[kb2][i], oacc[e]);
-            aacc[e] = E::mfma(dvf, sacc[kb2][i], aacc[e]);
-            bacc[e] = E::mfma(vf, dsacc[kb2][i], bacc[e]);
-          }
-        }
-    }
-  };
-
-  // Does the tile at key k0 need element masks?  Only the key tail, and in
-  // the frame-window case a tile not wholly inside the block's common window
-  // or an anchor frame.
-  auto needs_mask = [&](int k0) __attribute__((always_inline)) {
-    const int kz = k0 + BN;
-    bool m = kz > N;
-    if constexpr (MASKED) {
-      const bool in_win = k0 >= win_lo && kz <= win_hi;
-      const bool in_first = p.mask.first && kz <= p.mask.tpf;
-      const bool in_last = p.mask.last && k0 >= (p.mask.frames - 1) * p.mask.tpf;
-      m = m || !(in_win || in_first || in_last);
-    }
-    return m;
-  };
-
-  // One tile of two 32-key steps a, b in stage G: wait for it, release the
-  // other stage to the copy of the next tile, then the steps.  At d = 128 the
-  // order puts independent work side by side: the scores of b next to the
-  // exponentials of a, the products of a next to the running max of b.  At
-  // d = 64 (half the MFMAs per step) the plain order measures faster.  The
-  // element masks sit behind a branch that is uniform over the tile, placed
-  // where the order already ends a block.
-  static_assert(BN == 2 * CK, "two steps per tile");
-  constexpr bool kOverlap = BF16 && D >= 128;
-  auto tile = [&](auto G_, int it) __attribute__((always_inline)) {
-    using C0 = std::integral_constant<int, 0>;
-    using C1 = std::integral_constant<int, 1>;
-    const int k0 = tile_at(tr, it) * BN;
-    const bool need = needs_mask(k0);
-    wait_vmem();
-    __syncthreads();   // tile `it` landed; every wave is done with tile it-1
-    if (it + 1 < ntile) copier.issue(tile_at(tr, it + 1) * BN, N, smem, 1 - decltype(G_)::value);
-    f32x4 sa[2], dsa[2], sb[2], dsb[2];
-    scores(G_, C0{}, sa, dsa);
-    if (need) apply_mask(k0, sa, dsa);
-    update_max(sa);
-    if constexpr (kOverlap) {
-      scores(G_, C1{}, sb, dsb);
-      softmax(sa, dsa);
-      // the exponentials of a are computed here, beside the scores of b, not
-      // sunk past the mask branch below
-      asm volatile("" ::"v"(sa[0]), "v"(sa[1]), "v"(dsa[0]), "v"(dsa[1]));
-      if (need) apply_mask(k0 + CK, sb, dsb);
-      accumulate(G_, C0{}, sa, dsa);
-    } else {
-      softmax(sa, dsa);
-      accumulate(G_, C0{}, sa, dsa);
-      scores(G_, C1{}, sb, dsb);
-      if (need) apply_mask(k0 + CK, sb, dsb);
-    }
-    update_max(sb);
-    softmax(sb, dsb);
-    accumulate(G_, C1{}, sb, dsb);
-  };
-
-  int it = 0;
-  for (; it + 1 < ntile; it += 2) {
-    tile(std::integral_constant<int, 0>{}, it);
-    tile(std::integral_constant<int, 1>{}, it + 1);
-  }
-  if (it < ntile) tile(std::integral_constant<int, 0>{}, it);
-
-  // ---- epilogue ----
-  const float l_tot = row_sum4(l_run);
-  const bool empty = !(l_tot > 0.f);
-  const float inv = empty ? 0.f : 1.f / l_tot;
-  const float mu = scale * row_sum4(r_run) * inv;   // dLSE
-  const float sinv = scale * inv;
-  if (qvalid) {
-    T *O = (T *)p.o + b * p.so[0] + h * p.so[1] + (int64_t)qrow * p.so[2];
-    T *dO = (T *)p.dout + b * p.so[0] + h * p.so[1] + (int64_t)qrow * p.so[2];
-    // each lane owns 4 consecutive d of its row per d block: one packed
-    // 8-byte (bf16) or 16-byte (float32) store per block and tensor
-    typedef T T4 __attribute__((ext_vector_type(4)));
-#pragma unroll
-    for (int e = 0; e < ND; ++e) {
-      const int d0 = 16 * e + 4 * lg;
-      T4 ov, dv;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float o = oacc[e][i] * inv;
-        ov[i] = (T)o;
-        dv[i] = (T)(fmaf(bacc[e][i], sinv, aacc[e][i] * inv) - mu * o);
-      }
-      *(T4 *)(O + d0) = ov;
-      *(T4 *)(dO + d0) = dv;
-    }
-    if (lg == 0) {
-      const int64_t ro = (int64_t)bh * N + qrow;
-      p.lse[ro] = empty ? -INFINITY : (m_run + log2f(l_tot)) * 0.69314718055994530942f;
-      p.dlse[ro] = mu;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Host side.
-// ---------------------------------------------------------------------------
-constexpr int kBlockN = 64;
-#ifndef ATTN_JVP_CK
-#define ATTN_JVP_CK 32
-#endif
+using attn_jvp::MaskDev;
+using attn_jvp::Params;
+using attn_jvp::Shape;
 
 struct Extent {
   uintptr_t lo, hi;
@@ -785,21 +74,28 @@ bool same3(const int64_t a[3], const int64_t b[3]) {
   return a[0] == b[0] && a[1] == b[1] && a[2] == b[2];
 }
 
-int check_mask(const attn_jvp_mask *mask, int N) {
-  if (mask == nullptr || mask->kind == ATTN_JVP_MASK_NONE) return ATTN_JVP_OK;
+bool mask_on(const attn_jvp_mask *mask) {
+  return mask != nullptr && mask->kind != ATTN_JVP_MASK_NONE;
+}
+
+// The frame window is a self-attention mask: queries and keys are the same
+// frames * tokens_per_frame tokens.
+int check_mask(const attn_jvp_mask *mask, int Nq, int Nkv) {
+  if (!mask_on(mask)) return ATTN_JVP_OK;
   if (mask->kind != ATTN_JVP_MASK_FRAME_WINDOW) return ATTN_JVP_EMASK;
   if (mask->frames < 1 || mask->tokens_per_frame < 1 || mask->chunk_frames < 1 ||
       mask->radius_chunks < 0)
     return ATTN_JVP_EMASK;
-  if ((int64_t)mask->frames * mask->tokens_per_frame != N) return ATTN_JVP_EMASK;
-  if (N >= (1 << 24)) return ATTN_JVP_EMASK;   // frame arithmetic range
+  if (Nq != Nkv) return ATTN_JVP_EMASK;
+  if ((int64_t)mask->frames * mask->tokens_per_frame != Nq) return ATTN_JVP_EMASK;
+  if (Nq >= (1 << 24)) return ATTN_JVP_EMASK;   // frame arithmetic range
   return ATTN_JVP_OK;
 }
 
 MaskDev to_dev(const attn_jvp_mask *mask) {
   MaskDev m;
   memset(&m, 0, sizeof(m));
-  if (mask == nullptr || mask->kind == ATTN_JVP_MASK_NONE) return m;
+  if (!mask_on(mask)) return m;
   m.kind = 1;
   m.frames = mask->frames;
   m.tpf = mask->tokens_per_frame;
@@ -814,17 +110,37 @@ MaskDev to_dev(const attn_jvp_mask *mask) {
   return m;
 }
 
+// Contiguous [B, H, N, d] strides of every tensor of a shape.
+attn_jvp_layout contiguous(const attn_jvp_shape &s) {
+  attn_jvp_layout L;
+  const int64_t nq = s.seqlen_q, nkv = s.seqlen_kv, dqk = s.head_dim_qk, dv = s.head_dim_v;
+  const int64_t q[3] = {s.heads * nq * dqk, nq * dqk, dqk};
+  const int64_t k[3] = {s.heads * nkv * dqk, nkv * dqk, dqk};
+  const int64_t v[3] = {s.heads * nkv * dv, nkv * dv, dv};
+  const int64_t o[3] = {s.heads * nq * dv, nq * dv, dv};
+  for (int i = 0; i < 3; ++i) {
+    L.q[i] = L.dq[i] = q[i];
+    L.k[i] = L.dk[i] = k[i];
+    L.v[i] = L.dv[i] = v[i];
+    L.o[i] = L.dout[i] = o[i];
+  }
+  return L;
+}
+
 int check_args(const void *Q, const void *K, const void *V, const void *dQ,
                const void *dK, const void *dV, void *O, void *dO, float *LSE,
-               float *dLSE, int B, int H, int N, int d, int dtype,
+               float *dLSE, const attn_jvp_shape *shape, int dtype,
                const attn_jvp_layout *L, const attn_jvp_mask *mask) {
-  if (!Q || !K || !V || !dQ || !dK || !dV || !O || !dO || !LSE || !dLSE || !L)
+  if (!Q || !K || !V || !dQ || !dK || !dV || !O || !dO || !LSE || !dLSE || !shape || !L)
     return ATTN_JVP_EINVAL;
-  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return ATTN_JVP_EINVAL;
+  const int B = shape->batch, H = shape->heads, Nq = shape->seqlen_q, Nkv = shape->seqlen_kv;
+  const int dqk = shape->head_dim_qk, dv = shape->head_dim_v;
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nkv <= 0 || dqk <= 0 || dv <= 0) return ATTN_JVP_EINVAL;
   if (dtype != ATTN_JVP_BF16 && dtype != ATTN_JVP_FP32) return ATTN_JVP_EINVAL;
-  if ((int64_t)B * H * ((N + kBlockM - 1) / kBlockM) > 0x7fffffffLL) return ATTN_JVP_EINVAL;
-  if (d != 64 && d != 128) return ATTN_JVP_EUNSUPPORTED;
-  if (dtype == ATTN_JVP_FP32 && d != 64) return ATTN_JVP_EUNSUPPORTED;
+  Shape sh;
+  if (!attn_jvp::shape_for(dtype == ATTN_JVP_BF16, dqk, dv, &sh)) return ATTN_JVP_EUNSUPPORTED;
+  if (mask_on(mask) && dqk != dv) return ATTN_JVP_EUNSUPPORTED;
+  if ((int64_t)B * H * ((Nq + sh.block_m - 1) / sh.block_m) > 0x7fffffffLL) return ATTN_JVP_EINVAL;
   if (!same3(L->q, L->dq) || !same3(L->k, L->dk) || !same3(L->v, L->dv) ||
       !same3(L->o, L->dout))
     return ATTN_JVP_ESTRIDE;
@@ -842,12 +158,12 @@ int check_args(const void *Q, const void *K, const void *V, const void *dQ,
   if ((uintptr_t)LSE % 4 != 0 || (uintptr_t)dLSE % 4 != 0) return ATTN_JVP_ESTRIDE;
   // outputs must not overlap inputs or each other
   const Extent in[6] = {
-      extent_of(Q, L->q, B, H, N, d, esize),  extent_of(K, L->k, B, H, N, d, esize),
-      extent_of(V, L->v, B, H, N, d, esize),  extent_of(dQ, L->q, B, H, N, d, esize),
-      extent_of(dK, L->k, B, H, N, d, esize), extent_of(dV, L->v, B, H, N, d, esize)};
-  const int64_t rows = (int64_t)B * H * N;
-  const Extent out[4] = {extent_of(O, L->o, B, H, N, d, esize),
-                         extent_of(dO, L->o, B, H, N, d, esize),
+      extent_of(Q, L->q, B, H, Nq, dqk, esize),   extent_of(K, L->k, B, H, Nkv, dqk, esize),
+      extent_of(V, L->v, B, H, Nkv, dv, esize),   extent_of(dQ, L->q, B, H, Nq, dqk, esize),
+      extent_of(dK, L->k, B, H, Nkv, dqk, esize), extent_of(dV, L->v, B, H, Nkv, dv, esize)};
+  const int64_t rows = (int64_t)B * H * Nq;
+  const Extent out[4] = {extent_of(O, L->o, B, H, Nq, dv, esize),
+                         extent_of(dO, L->o, B, H, Nq, dv, esize),
                          Extent{(uintptr_t)LSE, (uintptr_t)LSE + (uintptr_t)(rows * 4)},
                          Extent{(uintptr_t)dLSE, (uintptr_t)dLSE + (uintptr_t)(rows * 4)}};
   for (int i = 0; i < 4; ++i) {
@@ -856,32 +172,84 @@ int check_args(const void *Q, const void *K, const void *V, const void *dQ,
     for (int j = i + 1; j < 4; ++j)
       if (overlaps(out[i], out[j])) return ATTN_JVP_ESTRIDE;
   }
-  return check_mask(mask, N);
+  return check_mask(mask, Nq, Nkv);
 }
 
-template <typename T, int D, bool MASKED>
-hipError_t launch(const Params &p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_jvp_kernel<T, D, kBlockN, ATTN_JVP_CK, MASKED>), dim3(grid),
-                     dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
+hipError_t dispatch(const Params &p, int dtype, int dqk, int dv, bool masked, hipStream_t s) {
+  if (dtype == ATTN_JVP_FP32) return attn_jvp::launch_fp32(p, dqk, dv, masked, s);
+  switch (dqk) {
+    case 16: return attn_jvp::launch_bf16_qk16(p, dv, masked, s);
+    case 32: return attn_jvp::launch_bf16_qk32(p, dv, masked, s);
+    case 64: return attn_jvp::launch_bf16_qk64(p, dv, masked, s);
+    case 128: return attn_jvp::launch_bf16_qk128(p, dv, masked, s);
+    case 256: return attn_jvp::launch_bf16_qk256(p, dv, masked, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
-template <typename T, int D>
-hipError_t launch_m(const Params &p, int grid, hipStream_t stream) {
-  return p.mask.kind ? launch<T, D, true>(p, grid, stream)
-                     : launch<T, D, false>(p, grid, stream);
+attn_jvp_shape square(int B, int H, int N, int d) {
+  attn_jvp_shape s;
+  s.batch = B;
+  s.heads = H;
+  s.seqlen_q = s.seqlen_kv = N;
+  s.head_dim_qk = s.head_dim_v = d;
+  return s;
 }
 
 }  // namespace
 
 extern "C" {
 
+int attn_jvp_check_ex(const void *Q, const void *K, const void *V, const void *dQ,
+                      const void *dK, const void *dV, void *O, void *dO, float *LSE,
+                      float *dLSE, const attn_jvp_shape *shape, int dtype,
+                      const attn_jvp_layout *layout, const attn_jvp_mask *mask) {
+  if (!shape) return ATTN_JVP_EINVAL;
+  const attn_jvp_layout L = layout ? *layout : contiguous(*shape);
+  return check_args(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, shape, dtype, &L, mask);
+}
+
+int attn_jvp_fwd_ex(const void *Q, const void *K, const void *V, const void *dQ,
+                    const void *dK, const void *dV, void *O, void *dO, float *LSE,
+                    float *dLSE, const attn_jvp_shape *shape, float scale, int dtype,
+                    const attn_jvp_layout *layout, const attn_jvp_mask *mask,
+                    void *stream) {
+  if (!shape) return ATTN_JVP_EINVAL;
+  const attn_jvp_layout L = layout ? *layout : contiguous(*shape);
+  const int st = check_args(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, shape, dtype, &L, mask);
+  if (st != ATTN_JVP_OK) return st;
+  Shape sh;
+  attn_jvp::shape_for(dtype == ATTN_JVP_BF16, shape->head_dim_qk, shape->head_dim_v, &sh);
+  Params p;
+  memset(&p, 0, sizeof(p));
+  p.q = Q; p.k = K; p.v = V; p.dq = dQ; p.dk = dK; p.dv = dV;
+  p.o = O; p.dout = dO; p.lse = LSE; p.dlse = dLSE;
+  for (int i = 0; i < 3; ++i) {
+    p.sq[i] = L.q[i];
+    p.sk[i] = L.k[i];
+    p.sv[i] = L.v[i];
+    p.so[i] = L.o[i];
+  }
+  p.B = shape->batch;
+  p.H = shape->heads;
+  p.Nq = shape->seqlen_q;
+  p.Nkv = shape->seqlen_kv;
+  p.nqb = (p.Nq + sh.block_m - 1) / sh.block_m;
+  p.scale = (scale > 0.f && isfinite(scale)) ? scale : 1.0f / sqrtf((float)shape->head_dim_qk);
+  p.scale_log2 = p.scale * 1.4426950408889634f;
+  p.mask = to_dev(mask);
+  const hipError_t err = dispatch(p, dtype, shape->head_dim_qk, shape->head_dim_v,
+                                  mask_on(mask), (hipStream_t)stream);
+  return err == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_EHIP;
+}
+
 int attn_jvp_check(const void *Q, const void *K, const void *V, const void *dQ,
                    const void *dK, const void *dV, void *O, void *dO, float *LSE,
                    float *dLSE, int B, int H, int N, int d, int dtype,
                    const attn_jvp_layout *layout, const attn_jvp_mask *mask) {
-  return check_args(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, B, H, N, d, dtype,
-                    layout, mask);
+  if (!layout) return ATTN_JVP_EINVAL;
+  const attn_jvp_shape s = square(B, H, N, d);
+  return check_args(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, &s, dtype, layout, mask);
 }
 
 int attn_jvp_fwd_strided(const void *Q, const void *K, const void *V,
@@ -890,55 +258,33 @@ int attn_jvp_fwd_strided(const void *Q, const void *K, const void *V,
                          int d, float scale, int dtype,
                          const attn_jvp_layout *layout, const attn_jvp_mask *mask,
                          void *stream) {
-  const int st = check_args(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, B, H, N, d,
-                            dtype, layout, mask);
-  if (st != ATTN_JVP_OK) return st;
-  Params p;
-  memset(&p, 0, sizeof(p));
-  p.q = Q; p.k = K; p.v = V; p.dq = dQ; p.dk = dK; p.dv = dV;
-  p.o = O; p.dout = dO; p.lse = LSE; p.dlse = dLSE;
-  for (int i = 0; i < 3; ++i) {
-    p.sq[i] = layout->q[i];
-    p.sk[i] = layout->k[i];
-    p.sv[i] = layout->v[i];
-    p.so[i] = layout->o[i];
-  }
-  p.B = B; p.H = H; p.N = N;
-  p.nqb = (N + kBlockM - 1) / kBlockM;
-  p.scale = (scale > 0.f && isfinite(scale)) ? scale : 1.0f / sqrtf((float)d);
-  p.scale_log2 = p.scale * 1.4426950408889634f;
-  p.mask = to_dev(mask);
-  const int grid = B * H * p.nqb;
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t err;
-  if (dtype == ATTN_JVP_BF16)
-    err = d == 128 ? launch_m<__bf16, 128>(p, grid, s) : launch_m<__bf16, 64>(p, grid, s);
-  else
-    err = launch_m<float, 64>(p, grid, s);
-  return err == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_EHIP;
+  if (!layout) return ATTN_JVP_EINVAL;
+  const attn_jvp_shape s = square(B, H, N, d);
+  return attn_jvp_fwd_ex(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, &s, scale, dtype, layout,
+                         mask, stream);
 }
 
 int attn_jvp_fwd(const void *Q, const void *K, const void *V, const void *dQ,
                  const void *dK, const void *dV, void *O, void *dO, float *LSE,
                  float *dLSE, int B, int H, int N, int d, float scale, int dtype,
                  const attn_jvp_mask *mask, void *stream) {
-  attn_jvp_layout L;
-  const int64_t s[3] = {(int64_t)H * N * d, (int64_t)N * d, (int64_t)d};
-  for (int i = 0; i < 3; ++i) {
-    L.q[i] = L.k[i] = L.v[i] = L.dq[i] = L.dk[i] = L.dv[i] = L.o[i] = L.dout[i] = s[i];
-  }
-  return attn_jvp_fwd_strided(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, B, H, N, d,
-                              scale, dtype, &L, mask, stream);
+  const attn_jvp_shape s = square(B, H, N, d);
+  return attn_jvp_fwd_ex(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, &s, scale, dtype, nullptr,
+                         mask, stream);
+}
+
+int attn_jvp_tile_shape_ex(int dtype, int d_qk, int d_v, int *block_m, int *block_n) {
+  if (!block_m || !block_n) return ATTN_JVP_EINVAL;
+  if (dtype != ATTN_JVP_BF16 && dtype != ATTN_JVP_FP32) return ATTN_JVP_EINVAL;
+  Shape sh;
+  if (!attn_jvp::shape_for(dtype == ATTN_JVP_BF16, d_qk, d_v, &sh)) return ATTN_JVP_EUNSUPPORTED;
+  *block_m = sh.block_m;
+  *block_n = sh.block_n;
+  return ATTN_JVP_OK;
 }
 
 int attn_jvp_tile_shape(int dtype, int d, int *block_m, int *block_n) {
-  if (!block_m || !block_n) return ATTN_JVP_EINVAL;
-  if (dtype != ATTN_JVP_BF16 && dtype != ATTN_JVP_FP32) return ATTN_JVP_EINVAL;
-  if (d != 64 && d != 128) return ATTN_JVP_EUNSUPPORTED;
-  if (dtype == ATTN_JVP_FP32 && d != 64) return ATTN_JVP_EUNSUPPORTED;
-  *block_m = kBlockM;
-  *block_n = kBlockN;
-  return ATTN_JVP_OK;
+  return attn_jvp_tile_shape_ex(dtype, d, d, block_m, block_n);
 }
 
 int attn_jvp_visible_tiles(int N, int dtype, int d, const attn_jvp_mask *mask,
@@ -947,14 +293,14 @@ int attn_jvp_visible_tiles(int N, int dtype, int d, const attn_jvp_mask *mask,
   const int st = attn_jvp_tile_shape(dtype, d, &bm, &bn);
   if (st != ATTN_JVP_OK) return st;
   if (N <= 0 || !tiles_per_block) return ATTN_JVP_EINVAL;
-  const int mst = check_mask(mask, N);
+  const int mst = check_mask(mask, N, N);
   if (mst != ATTN_JVP_OK) return mst;
   const MaskDev m = to_dev(mask);
   const int nqb = (N + bm - 1) / bm;
   for (int qb = 0; qb < nqb; ++qb) {
     const int q0 = qb * bm;
     const int q1 = q0 + bm < N ? q0 + bm : N;
-    const TileRanges tr = visible_tiles(m, q0, q1, N, bn);
+    const attn_jvp::TileRanges tr = attn_jvp::visible_tiles(m, q0, q1, N, bn);
     int64_t c = 0;
     for (int i = 0; i < tr.n; ++i) c += tr.hi[i] - tr.lo[i];
     tiles_per_block[qb] = c;
@@ -966,7 +312,7 @@ const char *attn_jvp_status_string(int status) {
   switch (status) {
     case ATTN_JVP_OK: return "ok";
     case ATTN_JVP_EINVAL: return "invalid argument (null pointer, size or dtype)";
-    case ATTN_JVP_EUNSUPPORTED: return "unsupported head dimension for this dtype";
+    case ATTN_JVP_EUNSUPPORTED: return "unsupported head dimensions for this dtype";
     case ATTN_JVP_ESTRIDE:
       return "bad layout (tangent strides differ from the primal's, misaligned "
              "pointer or stride, or outputs overlapping inputs)";

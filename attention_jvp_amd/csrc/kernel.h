@@ -1,0 +1,831 @@
+// Fused attention forward-mode derivative (JVP) for AMD gfx950 (MI355X):
+// the device code, shared by the instantiation units.
+//
+// What is computed (page "带分数正则的一致性蒸馏", gitcode.csdn.net, section
+// 注意力): per query row, O = softmax(s Q K^T) V together with its tangent
+// dO = P dV + (P (.) dS) V - rowsum(P (.) dS) O, dS = s (dQ K^T + Q dK^T), the
+// natural-log row log-sum-exp and its tangent.  The pages stream K/V blocks
+// with an online max m, sum l, tangent sum r and accumulators O~, A~ = P~ dV,
+// B~ = H~ V (H~ = P~ (.) dS); the kernel keeps all three and combines A~ and
+// B~ only in the epilogue (B~ carries dS without the scale).  Q, dQ are
+// [.., Lq, d_qk], K, dK [.., Lkv, d_qk], V, dV [.., Lkv, d_v], O, dO
+// [.., Lq, d_v] (the pages' op contract allows Lq != Lkv and d_qk != d_v).
+//
+// gfx950 design (one workgroup = W waves x 16 query rows of one (b, h)):
+//   * every wave owns 16 query rows and computes the TRANSPOSED score tile
+//     S^T = K Q^T with 16x16 MFMAs: lane l holds 4 keys of query l % 16, so
+//     the row max and row sums need one butterfly over the four lanes of a
+//     row (v_permlane16/32_swap), and the rounded scores are directly the B
+//     operand of the value products;
+//   * Q and dQ stay in registers (B operands) for the whole key loop;
+//   * K, dK, V, dV tiles move global -> LDS with asynchronous
+//     global_load_lds_dwordx4 copies into two LDS stages (the next tile
+//     streams in while the current one is consumed; no register staging),
+//     row-major with an XOR swizzle of the 16-byte chunks (one rule for the
+//     operand-row reads of K and dK, one for the transposing reads of V, dV);
+//   * the value products need V and dV transposed (keys along the MFMA k
+//     dimension): ds_read_b64_tr_b16 transposes on the way out of LDS;
+//   * O^T, A^T, B^T accumulate in 16x16 fp32 fragments that belong to the
+//     lane's own query, so the online rescale is one multiply by a per-lane
+//     factor, skipped unless the row max grew by more than 2^8;
+//   * exp2 domain for the scores (scale * log2 e folded into one FMA), the
+//     tangent stays in natural units;
+//   * workgroup ids are remapped so that all query blocks of one (b, h) land
+//     on the same XCD (dispatch round-robins consecutive ids over the 8 XCDs),
+//     keeping that head's K/V/dK/dV in one L2;
+//   * with a frame-window mask, each query block walks only the key-tile
+//     ranges some of its rows can see; element masks run on partial tiles.
+// Eight waves (two per SIMD) when the resident registers allow it, else four;
+// 64-key tiles when two stages fit in 128 KiB of LDS, else 32-key tiles.
+// float32 inputs use the same structure with v_mfma_f32_16x16x4_f32.
+
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <type_traits>
+
+namespace attn_jvp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kWaveRows = 16;   // query rows per wave
+constexpr int kStepKeys = 32;   // keys per softmax step
+
+// ---------------------------------------------------------------------------
+// Launch shape of one (dtype, d_qk, d_v) instance.
+// ---------------------------------------------------------------------------
+template <typename T, int DQK, int DV>
+struct Cfg {
+  static constexpr int ES = (int)sizeof(T);
+  static constexpr int RBK = DQK * ES;   // bytes per K / dK row
+  static constexpr int RBV = DV * ES;    // bytes per V / dV row
+  // VGPRs per lane that stay resident: Q and dQ fragments, O, A, B blocks.
+  // Two waves per SIMD (256 VGPRs each) while they leave room for the step's
+  // working set; float32 score steps need more of it (one k-step per 4 d).
+  static constexpr int kResident = (ES == 2 ? DQK / 4 : DQK / 2) + 3 * DV / 4;
+  static constexpr int kWaves = kResident <= (ES == 2 ? 128 : 64) ? 8 : 4;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kBlockM = kWaveRows * kWaves;
+  static constexpr int kBN = 4 * 64 * (RBK + RBV) <= 128 * 1024 ? 64 : 32;
+  static constexpr int kLds = 4 * kBN * (RBK + RBV);   // two stages of K, dK, V, dV
+};
+
+// ---------------------------------------------------------------------------
+// MFMA traits.  For an operand tile with 16 rows (or columns) and K along the
+// contraction, lane l holds row l % 16 and the K slice of lane group l / 16;
+// the 16x16 result puts column l % 16 and rows 4 (l / 16) + 0..3 in lane l.
+// ElemK contracts over the head dim (scores), ElemV over keys (values).
+// ---------------------------------------------------------------------------
+template <typename T, int DQK> struct ElemK;
+
+template <int DQK> struct ElemK<__bf16, DQK> {
+  using Frag = bf16x8;            // 8 bf16 along K per lane
+  static constexpr int KL = 8;    // K elements per lane
+  static constexpr int KI = 32;   // K per instruction (four lane groups)
+  __device__ static inline f32x4 mfma(Frag a, Frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct ElemK<__bf16, 16> {
+  using Frag = bf16x4;
+  static constexpr int KL = 4;
+  static constexpr int KI = 16;
+  __device__ static inline f32x4 mfma(Frag a, Frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  }
+};
+
+template <int DQK> struct ElemK<float, DQK> {
+  using Frag = float;
+  static constexpr int KL = 1;
+  static constexpr int KI = 4;
+  __device__ static inline f32x4 mfma(Frag a, Frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+
+template <typename T> struct ElemV;
+
+template <> struct ElemV<__bf16> {
+  using Frag = bf16x8;
+  __device__ static inline f32x4 mfma(Frag a, Frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct ElemV<float> {
+  using Frag = float;
+  __device__ static inline f32x4 mfma(Frag a, Frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Frame-window mask (page "VDN-Minimax-H3 ... Stage A1", yfxerp.com).
+// ---------------------------------------------------------------------------
+struct MaskDev {
+  int kind;        // 0 none, 1 frame window
+  int frames, tpf, chunk, radius;
+  int first, last, see_all;
+  float inv_tpf, inv_chunk;
+};
+
+// floor(n / den) for 0 <= n < 2^24 from a float estimate and exact fix-up.
+__host__ __device__ inline int div_fix(int n, int den, float inv) {
+  int q = (int)((float)n * inv);
+  q -= (q * den > n);
+  q -= (q * den > n);
+  q += ((q + 1) * den <= n);
+  q += ((q + 1) * den <= n);
+  return q;
+}
+
+struct TileRanges {
+  int n;
+  int lo[3], hi[3];   // key-tile index ranges [lo, hi), ascending, disjoint
+};
+
+// Key-tile ranges that some query of rows [q_lo, q_hi) can see.
+__host__ __device__ inline TileRanges visible_tiles(const MaskDev &m, int q_lo,
+                                                    int q_hi, int N, int BN) {
+  TileRanges tr;
+  const int ntiles = (N + BN - 1) / BN;
+  tr.n = 1;
+  tr.lo[0] = 0;
+  tr.hi[0] = ntiles;
+  tr.lo[1] = tr.hi[1] = tr.lo[2] = tr.hi[2] = 0;
+  if (m.kind == 0) return tr;
+  const int T = m.tpf, C = m.chunk, F = m.frames, R = m.radius;
+  const int qf0 = q_lo / T, qf1 = (q_hi - 1) / T;
+  if (m.see_all && ((m.first && qf0 == 0) || (m.last && qf1 == F - 1))) return tr;
+  const int c0 = qf0 / C, c1 = qf1 / C;
+  long long f_lo_l = (long long)(c0 - R) * C;
+  const int f_lo = f_lo_l < 0 ? 0 : (int)f_lo_l;
+  long long f_hi_l = (long long)(c1 + R + 1) * C;
+  int f_hi = f_hi_l > F ? F : (int)f_hi_l;
+  // candidate key-tile intervals in ascending order of start: first-frame
+  // anchor, chunk window, last-frame anchor; merged where they touch
+  // (static indices only, so nothing is spilled to memory)
+  tr.n = 0;
+  tr.lo[0] = tr.hi[0] = tr.lo[1] = tr.hi[1] = tr.lo[2] = tr.hi[2] = 0;
+  const bool valid[3] = {m.first != 0, true, m.last != 0};
+  const int a_[3] = {0, f_lo * T / BN, (F - 1) * T / BN};
+  const int z_[3] = {(T + BN - 1) / BN, (f_hi * T + BN - 1) / BN, (F * T + BN - 1) / BN};
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    if (!valid[i]) continue;
+    const int a = a_[i], z = z_[i];
+    if (tr.n == 0) {
+      tr.lo[0] = a; tr.hi[0] = z; tr.n = 1;
+    } else if (tr.n == 1) {
+      if (a <= tr.hi[0]) tr.hi[0] = z > tr.hi[0] ? z : tr.hi[0];
+      else { tr.lo[1] = a; tr.hi[1] = z; tr.n = 2; }
+    } else {
+      if (a <= tr.hi[1]) tr.hi[1] = z > tr.hi[1] ? z : tr.hi[1];
+      else { tr.lo[2] = a; tr.hi[2] = z; tr.n = 3; }
+    }
+  }
+  return tr;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel parameters.
+// ---------------------------------------------------------------------------
+struct Params {
+  const void *q, *k, *v, *dq, *dk, *dv;
+  void *o, *dout;
+  float *lse, *dlse;
+  int64_t sq[3], sk[3], sv[3], so[3];   // (b, h, n) element strides
+  int B, H, Nq, Nkv;
+  int nqb;                              // query blocks per (b, h)
+  float scale, scale_log2;
+  MaskDev mask;
+};
+
+__device__ inline int logical_block_id() {
+  // Dispatch places workgroup w on XCD (w mod 8).  Give each XCD a
+  // contiguous run of logical ids so a head's query blocks share one L2.
+  const int w = blockIdx.x, n = gridDim.x;
+  const int per = n / 8, rem = n % 8;
+  const int x = w % 8, local = w / 8;
+  return x * per + (x < rem ? x : rem) + local;
+}
+
+// ---------------------------------------------------------------------------
+// LDS tile layout.  A K or dK tile is BN rows of RB = d_qk * sizeof(T) bytes,
+// a V or dV tile BN rows of d_v * sizeof(T), row-major (one key per row).
+// The 16-byte chunks of row r are XOR-permuted, with one rule for the tiles
+// read as MFMA operand rows (K, dK) and another for the tiles read by
+// transposing loads (V, dV).  A 256-byte bank sweep holds RPB rows (or one
+// row's first 16 chunks):
+//  * K side, kswz(r): the row's sweep index mod the chunks per sweep.  16
+//    consecutive rows read at one logical chunk then fill every 16-byte slot
+//    of a sweep once.
+//  * V side, vswz(r): 8 consecutive rows, each read as a 32-byte run by four
+//    lanes of a transpose load, touch every bank once.
+// Both rules repeat every 16 rows, so a row offset that is a multiple of 16
+// keeps a lane's swizzle.
+// ---------------------------------------------------------------------------
+template <int RB>
+struct Sweep {
+  static constexpr int CPR = RB / 16;                 // chunks per row
+  static constexpr int RPB = RB >= 256 ? 1 : 256 / RB; // rows per bank sweep
+  static constexpr int CW = CPR < 16 ? CPR : 16;       // chunks per sweep per row
+};
+
+template <int RB>
+__device__ inline int kswz(int r) {
+  return (r / Sweep<RB>::RPB) % Sweep<RB>::CW;
+}
+
+template <int RB>
+__device__ inline int vswz(int r) {
+  constexpr int H = Sweep<RB>::CW / 2;
+  const int m = r / Sweep<RB>::RPB;
+  return ((m % H) << 1) | ((m / H) % 2);
+}
+
+template <int RB, bool KSIDE>
+__device__ inline int lds_off(int r, int byte_col) {
+  const int x = KSIDE ? kswz<RB>(r) : vswz<RB>(r);
+  return r * RB + ((((byte_col >> 4) ^ x)) << 4) + (byte_col & 15);
+}
+
+// Read 4 consecutive-key bf16 values of one d column: ds_read_b64_tr_b16.
+// In each 16-lane group, lane i receives element (i % 4) of the 8-byte chunks
+// addressed by lanes i/4, i/4 + 4, i/4 + 8 and i/4 + 12 (in that order).
+//
+// Issued through inline asm: the compiler cannot tell that these reads never
+// touch the LDS stage an in-flight global->LDS copy is filling, and would
+// otherwise wait for every outstanding copy (vmcnt(0)) before the first one,
+// serialising the tile prefetch.  The compiler does not count these reads, so
+// lds_tr_wait() must run before their results are used; extra LDS operations
+// it does not know about only make its own lgkmcnt waits stronger, since LDS
+// operations complete in issue order.
+template <int OFF>
+__device__ inline i16x4 lds_read_tr(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "DS offset field");
+  i16x4 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
+  return v;
+}
+
+__device__ inline uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __attribute__((always_inline)) inline void static_for(F &&f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Wait until at most N LDS operations are outstanding; the four values pass
+// through the asm so that nothing reading them can be scheduled before it.
+template <int N>
+__device__ inline void lds_tr_wait(i16x4 &a, i16x4 &b, i16x4 &c, i16x4 &d) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "n"(N));
+}
+
+// Sum and maximum over the four lanes l, l^16, l^32, l^48 that hold one
+// query row.  v_permlane16_swap(x, x) returns rows (x0, x0, x2, x2) and
+// (x1, x1, x3, x3) of x's four 16-lane rows, and v_permlane32_swap(x, x)
+// returns halves (lo, lo) and (hi, hi): combining the pair is one butterfly
+// step, done in the VALU without an LDS round trip.  Every lane of the row
+// ends with the same bits (same operand order on both sides).
+__device__ inline float row_sum4(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const unsigned v = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ inline float row_max4(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const unsigned v = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Asynchronous global->LDS copies of the key tiles of one side (K and dK, or
+// V and dV: two tensors with one row width RB).  Each wave instruction fills
+// 1 KiB of LDS contiguously, lane l writing bytes [16 l, 16 l + 16); the
+// lane picks the global chunk that the swizzled layout puts there.  The
+// per-lane byte offsets inside a tile are fixed, so they are computed once; a
+// tile then only moves the (scalar) base pointers.  The NI instructions of a
+// tensor tile go round-robin over the W waves.  Rows past the end of the
+// sequence re-read row N-1 (their scores are masked to -inf and their
+// tangents to 0).
+template <typename T, int RB, int BN, int W, bool KSIDE>
+struct SideCopier {
+  static constexpr int CPR = RB / 16;
+  static constexpr int TILE = BN * RB;
+  static constexpr int NI = TILE / 1024;
+  static constexpr int IPW = (NI + W - 1) / W;
+  static_assert(NI * 1024 == TILE, "a tile is whole 1 KiB wave copies");
+
+  const char *base[2];      // byte base of the two tensors for this (b, h)
+  int64_t rstride;          // row stride in bytes (shared by the two)
+  uint32_t rs;              // the same, 32-bit (below 2^24, checked on the host)
+  uint32_t slot[IPW];       // (row << 16) | swizzled chunk, per lane
+  int wave;                 // wave index (uniform)
+
+  __device__ void init(const T *t0, const T *t1, int64_t stride, int wave_, int lane) {
+    wave = wave_;
+    base[0] = (const char *)t0;
+    base[1] = (const char *)t1;
+    rstride = stride * (int64_t)sizeof(T);
+    rs = (uint32_t)rstride;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int s = (i * W + wave) * 64 + lane;
+      const int r = s / CPR;
+      const int c = (s % CPR) ^ (KSIDE ? kswz<RB>(r) : vswz<RB>(r));
+      slot[i] = ((uint32_t)r << 16) | (uint32_t)c;
+    }
+  }
+
+  // LDS: tensor t of stage g at dst0 + t * tstride (dst0 already holds g)
+  __device__ void issue(int k0, int N, char *dst0, int tstride) const {
+    const int valid = (N - k0 < BN ? N - k0 : BN) - 1;   // last real row
+    const char *tb0 = base[0] + (int64_t)k0 * rstride;
+    const char *tb1 = base[1] + (int64_t)k0 * rstride;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      if (NI % W != 0 && i * W + wave >= NI) break;   // uniform per wave
+      uint32_t r = slot[i] >> 16;
+      r = r < (uint32_t)valid ? r : (uint32_t)valid;
+      const uint32_t off = __umul24(r, rs) + ((slot[i] & 0xffffu) << 4);
+      char *dst = dst0 + (i * W + wave) * 1024;
+      __builtin_amdgcn_global_load_lds((const void *)(tb0 + off), (lds_void *)dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(tb1 + off), (lds_void *)(dst + tstride),
+                                       16, 0, 0);
+    }
+  }
+};
+
+__device__ inline void wait_vmem() {
+  // s_waitcnt vmcnt(0): every global->LDS copy this wave issued has landed
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// Tile index of the idx-th visited tile.
+__device__ inline int tile_at(const TileRanges &tr, int idx) {
+  int t = tr.lo[0] + idx;
+  if (tr.n > 1 && t >= tr.hi[0]) {
+    t = tr.lo[1] + (t - tr.hi[0]);
+    if (tr.n > 2 && t >= tr.hi[1]) t = tr.lo[2] + (t - tr.hi[1]);
+  }
+  return t;
+}
+
+// Lazy rescale: the running max only moves when a step's max exceeds it by
+// more than 2^8 (P~ then stays below 256); the final normalisation uses the
+// same reference, so the result is unchanged.
+constexpr float kRescaleThreshold = 8.0f;
+
+template <typename T, int DQK, int DV, bool MASKED>
+__global__ __launch_bounds__((Cfg<T, DQK, DV>::kThreads), 1) void attn_jvp_kernel(Params p) {
+  using C = Cfg<T, DQK, DV>;
+  using EK = ElemK<T, DQK>;
+  using EV = ElemV<T>;
+  using FragK = typename EK::Frag;
+  using FragV = typename EV::Frag;
+  constexpr bool BF16 = sizeof(T) == 2;
+  constexpr int W = C::kWaves;
+  constexpr int BN = C::kBN;
+  constexpr int CK = kStepKeys;
+  constexpr int NSTEP = BN / CK;              // 32-key steps per tile: 1 or 2
+  constexpr int KL = EK::KL;
+  constexpr int KI = EK::KI;
+  constexpr int RBK = C::RBK, RBV = C::RBV;   // bytes per LDS row
+  constexpr int TK = BN * RBK, TV = BN * RBV; // bytes per tensor tile
+  constexpr int VB = 4 * TK;                  // V-side region: after K, dK stages
+  constexpr int DS = DQK / KI;                // k-steps over d_qk
+  constexpr int ND = DV / 16;                 // 16-wide d_v blocks
+  static_assert(NSTEP == 1 || NSTEP == 2, "tile shape");
+  static_assert(DQK % KI == 0 && DV % 16 == 0, "head dims");
+
+  __shared__ __attribute__((aligned(1024))) char smem[C::kLds];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+  const int qi = lane & 15;        // this lane's query within the wave
+  const int lg = lane >> 4;        // lane group 0..3
+
+  const int lid = logical_block_id();
+  const int bh = lid / p.nqb;
+  const int qb = lid - bh * p.nqb;
+  const int b = bh / p.H;
+  const int h = bh - b * p.H;
+  const int Nq = p.Nq, Nkv = p.Nkv;
+
+  const T *Q = (const T *)p.q + b * p.sq[0] + h * p.sq[1];
+  const T *dQ = (const T *)p.dq + b * p.sq[0] + h * p.sq[1];
+
+  const int q0 = qb * C::kBlockM;
+  const int q_hi = (q0 + C::kBlockM < Nq) ? q0 + C::kBlockM : Nq;
+
+  TileRanges tr;
+  if constexpr (MASKED) {
+    tr = visible_tiles(p.mask, q0, q_hi, Nkv, BN);
+  } else {
+    tr.n = 1;
+    tr.lo[0] = 0;
+    tr.hi[0] = (Nkv + BN - 1) / BN;
+    tr.lo[1] = tr.hi[1] = tr.lo[2] = tr.hi[2] = 0;
+  }
+  // unused ranges are empty (lo = hi = 0)
+  const int ntile = (tr.hi[0] - tr.lo[0]) + (tr.hi[1] - tr.lo[1]) + (tr.hi[2] - tr.lo[2]);
+
+  // first tile in flight before anything else
+  SideCopier<T, RBK, BN, W, true> kcopy;
+  SideCopier<T, RBV, BN, W, false> vcopy;
+  kcopy.init((const T *)p.k + b * p.sk[0] + h * p.sk[1],
+             (const T *)p.dk + b * p.sk[0] + h * p.sk[1], p.sk[2], wave, lane);
+  vcopy.init((const T *)p.v + b * p.sv[0] + h * p.sv[1],
+             (const T *)p.dv + b * p.sv[0] + h * p.sv[1], p.sv[2], wave, lane);
+  auto issue_tile = [&](int it, int g) __attribute__((always_inline)) {
+    const int k0 = tile_at(tr, it) * BN;
+    kcopy.issue(k0, Nkv, smem + g * TK, 2 * TK);
+    vcopy.issue(k0, Nkv, smem + VB + g * TV, 2 * TV);
+  };
+  if (ntile > 0) issue_tile(0, 0);
+
+  const int qrow = q0 + wave * kWaveRows + qi;
+  const bool qvalid = qrow < Nq;
+
+  // ---- Q, dQ fragments (B operands of S^T = K Q^T), resident ----
+  FragK qf[DS], dqf[DS];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) {
+    if (qvalid) {
+      const int64_t off = (int64_t)qrow * p.sq[2] + s * KI + lg * KL;
+      qf[s] = *(const FragK *)(Q + off);
+      dqf[s] = *(const FragK *)(dQ + off);
+    } else {
+      qf[s] = FragK{};
+      dqf[s] = FragK{};
+    }
+  }
+
+  // O^T, A^T = (P~ dV)^T and B^T = ((P~ . dS) V)^T blocks (dS without the
+  // scale, applied once in the epilogue): lane holds d = 16e + 4 lg + 0..3 of
+  // query qi.  The row sums l (of P~) and r (of P~ . dS) are taken in fp32
+  // before the bf16 rounding, lane-partial until the epilogue.
+  f32x4 oacc[ND], aacc[ND], bacc[ND];
+#pragma unroll
+  for (int e = 0; e < ND; ++e) {
+    oacc[e] = f32x4{};
+    aacc[e] = f32x4{};
+    bacc[e] = f32x4{};
+  }
+  float l_run = 0.f, r_run = 0.f;
+  float m_run = -INFINITY;   // reference max, log2 units
+
+  const float scale = p.scale;
+  const float c2 = p.scale_log2;
+
+  // Query-side mask terms.  Chunks are runs of whole frames, so the keys
+  // this lane's query sees by the chunk rule form one interval
+  // [kv_lo, kv_hi); the anchor frames add [0, a_first_hi) and
+  // [a_last_lo, N).  Keys in [win_lo, win_hi) and the anchor frames are
+  // visible to every row of the block, so tiles inside them need no mask.
+  int kv_lo = 0, kv_hi = Nkv, a_first_hi = 0, a_last_lo = Nkv;
+  int win_lo = 0, win_hi = 0;
+  if constexpr (MASKED) {
+    const long long F = p.mask.frames, TPF = p.mask.tpf, CH = p.mask.chunk, R = p.mask.radius;
+    const int qf_ = div_fix(qvalid ? qrow : 0, p.mask.tpf, p.mask.inv_tpf);
+    const int q_chunk = div_fix(qf_, p.mask.chunk, p.mask.inv_chunk);
+    const bool q_all = p.mask.see_all &&
+                       ((p.mask.first && qf_ == 0) || (p.mask.last && qf_ == p.mask.frames - 1));
+    long long flo = (q_chunk - R) * CH, fhi = (q_chunk + R + 1) * CH;
+    flo = flo < 0 ? 0 : flo;
+    fhi = fhi > F ? F : fhi;
+    if (!q_all) {
+      kv_lo = (int)(flo * TPF);
+      kv_hi = fhi > flo ? (int)(fhi * TPF) : kv_lo;
+    }
+    a_first_hi = p.mask.first ? (int)TPF : 0;
+    a_last_lo = p.mask.last ? (int)((F - 1) * TPF) : Nkv;
+    // the rows of the whole block: chunks c0..c1
+    const long long c0 = (q0 / TPF) / CH;
+    const long long c1 = ((q_hi - 1) / TPF) / CH;
+    long long wlo = (c1 - R) * CH, whi = (c0 + R + 1) * CH;
+    wlo = wlo < 0 ? 0 : wlo;
+    whi = whi > F ? F : whi;
+    if (whi > wlo) {
+      win_lo = (int)(wlo * TPF);
+      win_hi = (int)(whi * TPF);
+    }
+  }
+
+  // Lane-dependent parts of the LDS addresses, fixed for the whole loop.
+  // Rows kb + 16 kb2 + qi (K operand) and kb + 16 u + 4 lg + qi / 4
+  // (transpose reads of V) have the swizzle of their row mod 16, so adding
+  // the step's row offset and the stage/tensor offset is a constant that goes
+  // into the instructions' offset field.
+  const uint32_t smem_a = lds_addr(smem);
+  uint32_t kl[DS];                          // K operand, k-step s
+#pragma unroll
+  for (int s = 0; s < DS; ++s)
+    kl[s] = smem_a + lds_off<RBK, true>(qi, (s * KI + lg * KL) * (int)sizeof(T));
+  uint32_t vl[BF16 ? ND : 1];               // V transpose reads, d block e
+  if constexpr (BF16) {
+#pragma unroll
+    for (int e = 0; e < ND; ++e)
+      vl[e] = smem_a + VB + lds_off<RBV, false>(4 * lg + (qi >> 2), (16 * e + 4 * (qi & 3)) * 2);
+  }
+
+  // ---- S^T and dS^T of 32-key step KC of the tile in stage G ----
+  // sacc[kb2][i] is the score of key kb + 16 kb2 + 4 lg + i for query qi
+  auto scores = [&](auto G_, auto KC_, f32x4 (&sacc)[2], f32x4 (&dsacc)[2])
+                    __attribute__((always_inline)) {
+    constexpr int G = decltype(G_)::value;
+    constexpr int kb = decltype(KC_)::value * CK;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      f32x4 s_ = f32x4{}, ds_ = f32x4{};
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        const char *kp = smem + (kl[s] - smem_a) + G * TK + (kb + 16 * kb2) * RBK;
+        const FragK kf = *(const FragK *)kp;
+        const FragK dkf = *(const FragK *)(kp + 2 * TK);
+        s_ = EK::mfma(kf, qf[s], s_);
+        ds_ = EK::mfma(kf, dqf[s], ds_);
+        ds_ = EK::mfma(dkf, qf[s], ds_);
+      }
+      sacc[kb2] = s_;
+      dsacc[kb2] = ds_;
+    }
+  };
+
+  // ---- element masks (key tail, partial frame-window tiles) ----
+  // ka is the first key of the step.  Straight-line selects: the visibility
+  // of every element is computed, with no per-lane branch.
+  auto apply_mask = [&](int ka, f32x4 (&sacc)[2], f32x4 (&dsacc)[2])
+                        __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = ka + 16 * kb2 + 4 * lg + i;
+        bool vis = key < Nkv;
+        if constexpr (MASKED) {
+          // bitwise, not short-circuit: no branch per element
+          const bool in_chunks = (unsigned)(key - kv_lo) < (unsigned)(kv_hi - kv_lo);
+          vis = vis & (in_chunks | (key < a_first_hi) | (key >= a_last_lo));
+        }
+        sacc[kb2][i] = vis ? sacc[kb2][i] : -INFINITY;
+        dsacc[kb2][i] = vis ? dsacc[kb2][i] : 0.f;
+      }
+    }
+  };
+
+  // ---- running max (log2 domain) and lazy rescale of the accumulators ----
+  // IEEE maximum (NaN-propagating): v_maximum3_f32, no canonicalisation
+  auto update_max = [&](const f32x4 (&sacc)[2]) __attribute__((always_inline)) {
+    const f32x4 m2 = __builtin_elementwise_maximum(sacc[0], sacc[1]);
+    float mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m2[0], m2[1]),
+                                             __builtin_elementwise_maximum(m2[2], m2[3]));
+    mx = row_max4(mx) * c2;
+    if (__any(mx > m_run + kRescaleThreshold)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+      r_run *= alpha;
+#pragma unroll
+      for (int e = 0; e < ND; ++e) {
+        oacc[e] *= alpha;
+        aacc[e] *= alpha;
+        bacc[e] *= alpha;
+      }
+      m_run = m_new;
+    }
+  };
+
+  // ---- P~ = exp2(S - m) and H = P~ . dS (in place), row sums l and r ----
+  auto softmax = [&](f32x4 (&sacc)[2], f32x4 (&dsacc)[2]) __attribute__((always_inline)) {
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][i], c2, -m_use));
+        const float hv = pv * dsacc[kb2][i];
+        l_run += pv;
+        r_run += hv;
+        sacc[kb2][i] = pv;
+        dsacc[kb2][i] = hv;
+      }
+    }
+  };
+
+  // ---- O^T += V^T P^T ; A^T += dV^T P^T ; B^T += V^T H^T, step KC, stage G ----
+  auto accumulate = [&](auto G_, auto KC_, const f32x4 (&sacc)[2], const f32x4 (&dsacc)[2])
+                        __attribute__((always_inline)) {
+    constexpr int G = decltype(G_)::value;
+    constexpr int kb = decltype(KC_)::value * CK;
+    if constexpr (BF16) {
+      // B operand: lane (query qi, group lg) gives keys 4lg + 0..3 and
+      // 16 + 4lg + 0..3 of the step, in that order
+      bf16x8 pf, hf;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pf[i] = (__bf16)sacc[0][i];
+        pf[4 + i] = (__bf16)sacc[1][i];
+        hf[i] = (__bf16)dsacc[0][i];
+        hf[4 + i] = (__bf16)dsacc[1][i];
+      }
+      // A operand for d block e: lane (d = 16e + qi, group lg) needs the same
+      // keys of V and dV -- four transpose reads.  Groups e+1 and e+2 are in
+      // flight while group e feeds its MFMAs.
+      constexpr int VO = G * TV + kb * RBV;          // stage and step rows
+      auto issue = [&](auto e_, i16x4 (&r)[4]) __attribute__((always_inline)) {
+        constexpr int e = decltype(e_)::value;
+        r[0] = lds_read_tr<VO>(vl[e]);
+        r[1] = lds_read_tr<VO + 16 * RBV>(vl[e]);
+        r[2] = lds_read_tr<VO + 2 * TV>(vl[e]);
+        r[3] = lds_read_tr<VO + 2 * TV + 16 * RBV>(vl[e]);
+      };
+      i16x4 buf[3][4];
+      issue(std::integral_constant<int, 0>{}, buf[0]);
+      if constexpr (ND > 1) issue(std::integral_constant<int, 1>{}, buf[1]);
+      static_for<0, ND>([&](auto e_) __attribute__((always_inline)) {
+        constexpr int e = decltype(e_)::value;
+        i16x4(&cur)[4] = buf[e % 3];
+        if constexpr (e + 2 < ND) {
+          issue(std::integral_constant<int, e + 2>{}, buf[(e + 2) % 3]);
+          lds_tr_wait<8>(cur[0], cur[1], cur[2], cur[3]);
+        } else if constexpr (e + 1 < ND) {
+          lds_tr_wait<4>(cur[0], cur[1], cur[2], cur[3]);
+        } else {
+          lds_tr_wait<0>(cur[0], cur[1], cur[2], cur[3]);
+        }
+        const FragV vf = __builtin_bit_cast(FragV, __builtin_shufflevector(cur[0], cur[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        const FragV dvf = __builtin_bit_cast(FragV, __builtin_shufflevector(cur[2], cur[3], 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[e] = EV::mfma(vf, pf, oacc[e]);
+        aacc[e] = EV::mfma(dvf, pf, aacc[e]);
+        bacc[e] = EV::mfma(vf, hf, bacc[e]);
+      });
+    } else {
+      // float32: k-step (kb2, i) takes key 16 kb2 + 4 lg + i from lane group lg
+      const char *Vs = smem + VB + G * TV;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kb + 16 * kb2 + 4 * lg + i;
+#pragma unroll
+          for (int e = 0; e < ND; ++e) {
+            const int o = lds_off<RBV, false>(key, (16 * e + qi) * 4);
+            const FragV vf = *(const FragV *)(Vs + o);
+            const FragV dvf = *(const FragV *)(Vs + 2 * TV + o);
+            oacc[e] = EV::mfma(vf, sacc[kb2][i], oacc[e]);
+            aacc[e] = EV::mfma(dvf, sacc[kb2][i], aacc[e]);
+            bacc[e] = EV::mfma(vf, dsacc[kb2][i], bacc[e]);
+          }
+        }
+    }
+  };
+
+  // Does the tile at key k0 need element masks?  Only the key tail, and in
+  // the frame-window case a tile not wholly inside the block's common window
+  // or an anchor frame.
+  auto needs_mask = [&](int k0) __attribute__((always_inline)) {
+    const int kz = k0 + BN;
+    bool m = kz > Nkv;
+    if constexpr (MASKED) {
+      const bool in_win = k0 >= win_lo && kz <= win_hi;
+      const bool in_first = p.mask.first && kz <= p.mask.tpf;
+      const bool in_last = p.mask.last && k0 >= (p.mask.frames - 1) * p.mask.tpf;
+      m = m || !(in_win || in_first || in_last);
+    }
+    return m;
+  };
+
+  // One tile in stage G: wait for it, release the other stage to the copy of
+  // the next tile, then its steps.  With two steps a, b and the larger head
+  // dims the order puts independent work side by side: the scores of b next
+  // to the exponentials of a, the products of a next to the running max of
+  // b; otherwise the plain order measures faster.  The element masks sit
+  // behind a branch that is uniform over the tile, placed where the order
+  // already ends a block.
+  constexpr bool kOverlap = BF16 && NSTEP == 2 && DQK + DV >= 256;
+  auto tile = [&](auto G_, int it) __attribute__((always_inline)) {
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    const int k0 = tile_at(tr, it) * BN;
+    const bool need = needs_mask(k0);
+    wait_vmem();
+    __syncthreads();   // tile `it` landed; every wave is done with tile it-1
+    if (it + 1 < ntile) issue_tile(it + 1, 1 - decltype(G_)::value);
+    f32x4 sa[2], dsa[2];
+    scores(G_, C0{}, sa, dsa);
+    if (need) apply_mask(k0, sa, dsa);
+    update_max(sa);
+    if constexpr (NSTEP == 1) {
+      softmax(sa, dsa);
+      accumulate(G_, C0{}, sa, dsa);
+    } else {
+      f32x4 sb[2], dsb[2];
+      if constexpr (kOverlap) {
+        scores(G_, C1{}, sb, dsb);
+        softmax(sa, dsa);
+        // the exponentials of a are computed here, beside the scores of b,
+        // not sunk past the mask branch below
+        asm volatile("" ::"v"(sa[0]), "v"(sa[1]), "v"(dsa[0]), "v"(dsa[1]));
+        if (need) apply_mask(k0 + CK, sb, dsb);
+        accumulate(G_, C0{}, sa, dsa);
+      } else {
+        softmax(sa, dsa);
+        accumulate(G_, C0{}, sa, dsa);
+        scores(G_, C1{}, sb, dsb);
+        if (need) apply_mask(k0 + CK, sb, dsb);
+      }
+      update_max(sb);
+      softmax(sb, dsb);
+      accumulate(G_, C1{}, sb, dsb);
+    }
+  };
+
+  int it = 0;
+  for (; it + 1 < ntile; it += 2) {
+    tile(std::integral_constant<int, 0>{}, it);
+    tile(std::integral_constant<int, 1>{}, it + 1);
+  }
+  if (it < ntile) tile(std::integral_constant<int, 0>{}, it);
+
+  // ---- epilogue ----
+  const float l_tot = row_sum4(l_run);
+  const bool empty = !(l_tot > 0.f);
+  const float inv = empty ? 0.f : 1.f / l_tot;
+  const float mu = scale * row_sum4(r_run) * inv;   // dLSE
+  const float sinv = scale * inv;
+  if (qvalid) {
+    T *O = (T *)p.o + b * p.so[0] + h * p.so[1] + (int64_t)qrow * p.so[2];
+    T *dO = (T *)p.dout + b * p.so[0] + h * p.so[1] + (int64_t)qrow * p.so[2];
+    // each lane owns 4 consecutive d of its row per d block: one packed
+    // 8-byte (bf16) or 16-byte (float32) store per block and tensor
+    typedef T T4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int e = 0; e < ND; ++e) {
+      const int d0 = 16 * e + 4 * lg;
+      T4 ov, dv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float o = oacc[e][i] * inv;
+        ov[i] = (T)o;
+        dv[i] = (T)(fmaf(bacc[e][i], sinv, aacc[e][i] * inv) - mu * o);
+      }
+      *(T4 *)(O + d0) = ov;
+      *(T4 *)(dO + d0) = dv;
+    }
+    if (lg == 0) {
+      const int64_t ro = (int64_t)bh * Nq + qrow;
+      p.lse[ro] = empty ? -INFINITY : (m_run + log2f(l_tot)) * 0.69314718055994530942f;
+      p.dlse[ro] = mu;
+    }
+  }
+}
+
+// Launch one instance: grid = B * H * ceil(Nq / block_m) workgroups.
+template <typename T, int DQK, int DV, bool MASKED>
+hipError_t launch_instance(const Params &p, hipStream_t stream) {
+  using C = Cfg<T, DQK, DV>;
+  const int grid = p.B * p.H * p.nqb;
+  hipLaunchKernelGGL((attn_jvp_kernel<T, DQK, DV, MASKED>), dim3(grid), dim3(C::kThreads), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+// Launch shape of (T, d_qk, d_v) for the host.
+struct Shape {
+  int waves, block_m, block_n;
+};
+
+template <typename T, int DQK, int DV>
+Shape shape_of() {
+  using C = Cfg<T, DQK, DV>;
+  return Shape{C::kWaves, C::kBlockM, C::kBN};
+}
+
+}  // namespace attn_jvp

@@ -26,7 +26,7 @@ METRIC = "attention-JVP TFLOP/s (fwd+tangent) and % of bf16 MFMA peak, 1 GPU"
 # MI355X dense MFMA peaks, TFLOP/s
 PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}
 NAMES = ("q", "k", "v", "dq", "dk", "dv")
-KERNEL_SOURCE = os.path.join(ROOT, "attention_jvp_amd", "csrc", "attn_jvp.hip")
+KERNEL_SOURCES = os.path.join(ROOT, "attention_jvp_amd", "csrc")
 
 
 def log(msg):
@@ -55,8 +55,14 @@ def visible_pairs(N, mask):
 
 
 def kernel_sha():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 over the kernel sources (every file of csrc/, by name)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_SOURCES)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(KERNEL_SOURCES, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
 
 
 def traffic_record(workload):

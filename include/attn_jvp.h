@@ -26,13 +26,18 @@
  * Conventions shared by every entry point:
  *   - Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE are DEVICE pointers owned by the
  *     caller; the library allocates and frees no device memory.
- *   - Tensors are logically [B, H, N, d] (queries and keys have the same N).
- *     The last (d) dimension must be contiguous; the other strides are
+ *   - Shapes follow the pages' op contract: Q, dQ are [B, H, Lq, d_qk];
+ *     K, dK are [B, H, Lkv, d_qk]; V, dV are [B, H, Lkv, d_v]; O, dO are
+ *     [B, H, Lq, d_v]; LSE, dLSE are [B, H, Lq].  The square entry points
+ *     (attn_jvp_fwd, attn_jvp_fwd_strided) take Lq = Lkv = N and
+ *     d_qk = d_v = d.  Built head dims: d_qk, d_v in {16, 32, 64, 128, 256}
+ *     for bfloat16 and {16, 32, 64} for float32 (others: EUNSUPPORTED).
+ *   - The last (d) dimension must be contiguous; the other strides are
  *     given in ELEMENTS.  Tangents must use exactly the strides of their
  *     primal (dQ of Q, dK of K, dV of V, dO of O), as the pages require.
  *   - Every row start must be 16-byte aligned: base pointers aligned to 16
  *     bytes and strides multiples of 8 elements (bf16) or 4 (float32).
- *   - LSE and dLSE are float32, contiguous [B, H, N].
+ *   - LSE and dLSE are float32, contiguous [B, H, Lq].
  *   - O, dO, LSE, dLSE must not alias any input.
  *   - The call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream).  Arguments are validated on the host before anything is
@@ -61,7 +66,8 @@ typedef enum {
 typedef enum {
   ATTN_JVP_OK = 0,
   ATTN_JVP_EINVAL = -1,      /* null pointer, non-positive size, bad dtype  */
-  ATTN_JVP_EUNSUPPORTED = -2,/* head dim not built (built: 64, 128)         */
+  ATTN_JVP_EUNSUPPORTED = -2,/* head dims not built for the dtype, or a
+                                frame-window mask with d_qk != d_v          */
   ATTN_JVP_ESTRIDE = -3,     /* tangent strides differ from the primal's, a
                                 misaligned pointer or stride, or overlap    */
   ATTN_JVP_EMASK = -4,       /* inconsistent mask descriptor                */
@@ -78,9 +84,10 @@ enum { ATTN_JVP_MASK_NONE = 0, ATTN_JVP_MASK_FRAME_WINDOW = 1 };
  *     |chunk(frame(i)) - chunk(frame(j))| <= radius_chunks
  *  or (anchor_first && frame(j) == 0) or (anchor_last && frame(j) == frames-1)
  *  or (anchor_queries_see_all && frame(i) is an enabled anchor frame).
- * Requires frames * tokens_per_frame == N, chunk_frames >= 1,
- * radius_chunks >= 0, otherwise ATTN_JVP_EMASK.  Every query sees its own
- * frame, so no row is empty.  Tiles of keys that no query of a query block
+ * Self-attention only: requires Lq == Lkv == N, frames * tokens_per_frame
+ * == N, chunk_frames >= 1, radius_chunks >= 0, otherwise ATTN_JVP_EMASK
+ * (and d_qk == d_v, otherwise ATTN_JVP_EUNSUPPORTED).  Every query sees its
+ * own frame, so no row is empty.  Tiles of keys that no query of a query block
  * can see are neither loaded nor computed. */
 typedef struct {
   int32_t kind;
@@ -99,6 +106,34 @@ typedef struct {
   int64_t dq[3], dk[3], dv[3];
   int64_t o[3], dout[3];
 } attn_jvp_layout;
+
+/* Sizes of one call (see the shape convention above). */
+typedef struct {
+  int32_t batch;       /* B */
+  int32_t heads;       /* H */
+  int32_t seqlen_q;    /* Lq: query rows */
+  int32_t seqlen_kv;   /* Lkv: key / value rows */
+  int32_t head_dim_qk; /* d_qk: head dim of Q, K, dQ, dK */
+  int32_t head_dim_v;  /* d_v: head dim of V, dV, O, dO */
+} attn_jvp_shape;
+
+/* General entry point: Lq may differ from Lkv (cross-attention, or a key
+ * range of a longer sequence) and d_qk from d_v.  `layout` NULL means every
+ * tensor is contiguous in its own shape.  scale <= 0 selects 1/sqrt(d_qk).
+ * Returns an attn_jvp_status; nothing is launched unless it is ATTN_JVP_OK. */
+int attn_jvp_fwd_ex(const void *Q, const void *K, const void *V,
+                    const void *dQ, const void *dK, const void *dV,
+                    void *O, void *dO, float *LSE, float *dLSE,
+                    const attn_jvp_shape *shape, float scale, int dtype,
+                    const attn_jvp_layout *layout, const attn_jvp_mask *mask,
+                    void *stream);
+
+/* Host-only argument check of attn_jvp_fwd_ex (never touches the GPU). */
+int attn_jvp_check_ex(const void *Q, const void *K, const void *V,
+                      const void *dQ, const void *dK, const void *dV,
+                      void *O, void *dO, float *LSE, float *dLSE,
+                      const attn_jvp_shape *shape, int dtype,
+                      const attn_jvp_layout *layout, const attn_jvp_mask *mask);
 
 /* Contiguous [B, H, N, d] tensors.  scale <= 0 selects 1/sqrt(d).
  * Returns an attn_jvp_status. */
@@ -127,8 +162,11 @@ int attn_jvp_check(const void *Q, const void *K, const void *V,
                    const attn_jvp_layout *layout, const attn_jvp_mask *mask);
 
 /* Host-only: the query-block rows (block_m) and key-tile length (block_n) the
- * library uses for (dtype, d); returns a status. */
+ * library uses for (dtype, d_qk = d_v = d); returns a status. */
 int attn_jvp_tile_shape(int dtype, int d, int *block_m, int *block_n);
+
+/* The same for unequal head dims (dtype, d_qk, d_v). */
+int attn_jvp_tile_shape_ex(int dtype, int d_qk, int d_v, int *block_m, int *block_n);
 
 /* Host-only: the key tiles the scheduler visits for each query block of an
  * N-token sequence under `mask` (NULL = dense) with the tile shape of

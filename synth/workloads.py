@@ -51,12 +51,23 @@ class Workload:
     tangents: str = "gaussian"    # "gaussian" or "trigflow"
     tangent_scale: float = 1.0
     mask: dict = field(default=None, hash=False, compare=False)
+    n_kv: int = None              # key/value rows (None: N, self-attention)
+    d_v: int = None               # value head dim (None: d)
+
+    @property
+    def Nkv(self):
+        return self.N if self.n_kv is None else self.n_kv
+
+    @property
+    def dv(self):
+        return self.d if self.d_v is None else self.d_v
 
     @property
     def flops(self):
-        """Counted FLOPs of the dense definition: 6 products of 2 N^2 d each
-        per (batch, head)."""
-        return 12.0 * self.B * self.H * self.N * self.N * self.d
+        """Counted FLOPs of the dense definition per (batch, head): three
+        products over d_qk (Q K^T, dQ K^T, Q dK^T) and three over d_v (P V,
+        P dV, (P . dS) V), 2 Lq Lkv d each; 12 N^2 d when square."""
+        return 6.0 * self.B * self.H * self.N * self.Nkv * (self.d + self.dv)
 
 
 FRAME_WINDOW_65520 = {
@@ -98,15 +109,22 @@ def _threads():
 
 
 def make_inputs(w, seed=None):
-    """Return a dict of CPU torch tensors q, k, v, dq, dk, dv ([B, H, N, d],
-    contiguous, in the workload dtype) plus ``scale`` (None = 1/sqrt(d)) and
-    ``mask`` (a frame-window dict or None)."""
+    """Return a dict of CPU torch tensors q, dq [B, H, N, d], k, dk [B, H,
+    Nkv, d], v, dv [B, H, Nkv, dv] (contiguous, in the workload dtype) plus
+    ``scale`` (None = 1/sqrt(d)) and ``mask`` (a frame-window dict or None)."""
     seed = w.seed if seed is None else seed
     tdt = _TORCH_DTYPE[w.dtype]
     B, H, N, d = w.B, w.H, w.N, w.d
-    out = {n: torch.empty((B, H, N, d), dtype=tdt) for n in ("q", "k", "v", "dq", "dk", "dv")}
+    rows = {"q": N, "k": w.Nkv, "v": w.Nkv}
+    cols = {"q": d, "k": d, "v": w.dv}
+    out = {}
+    for n in ("q", "k", "v"):
+        out[n] = torch.empty((B, H, rows[n], cols[n]), dtype=tdt)
+        out["d" + n] = torch.empty((B, H, rows[n], cols[n]), dtype=tdt)
 
     if w.tangents == "trigflow":
+        if w.Nkv != N or w.dv != d:
+            raise ValueError("the TrigFlow tangent recipe is for self-attention shapes")
         t = float(_rng(seed, _ID["t"]).uniform(0.0, math.pi / 2))
         wmat = {n: _rng(seed, _ID["w" + n]).standard_normal((d, d)) / math.sqrt(d)
                 for n in ("q", "k", "v")}
@@ -116,7 +134,7 @@ def make_inputs(w, seed=None):
     def slab(bh):
         b, h = divmod(bh, H)
         for n in ("q", "k", "v"):
-            x = _rng(seed, _ID[n], b, h).standard_normal((N, d))
+            x = _rng(seed, _ID[n], b, h).standard_normal((rows[n], cols[n]))
             if w.rms_qk and n in ("q", "k"):
                 x = _rms_normalise(x)
             out[n][b, h] = torch.from_numpy(x).to(tdt)
@@ -128,7 +146,7 @@ def make_inputs(w, seed=None):
                 out["d" + n][b, h] = torch.from_numpy(dx @ wmat[n]).to(tdt)
         else:
             for n in ("dq", "dk", "dv"):
-                x = _rng(seed, _ID[n], b, h).standard_normal((N, d)) * w.tangent_scale
+                x = _rng(seed, _ID[n], b, h).standard_normal((rows[n[1]], cols[n[1]])) * w.tangent_scale
                 out[n][b, h] = torch.from_numpy(x).to(tdt)
 
     with ThreadPoolExecutor(_threads()) as ex:

@@ -55,15 +55,18 @@ def _check(B=1, H=2, N=100, d=128, dtype=0, lay=None, mask=None, ptrs=None):
 
 def test_valid_arguments():
     assert _check() == 0
-    assert _check(d=64) == 0
-    assert _check(d=64, dtype=1) == 0
+    for d in (16, 32, 64, 256):
+        assert _check(d=d) == 0, d
+    for d in (16, 32, 64):
+        assert _check(d=d, dtype=1) == 0, d
     assert _check(N=65520, H=1, mask=dict(frames=42, tokens_per_frame=1560, chunk_frames=5,
                                           radius_chunks=1)) == 0
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(B=0), -1), (dict(H=-1), -1), (dict(N=0), -1), (dict(dtype=7), -1),
-    (dict(d=96), -2), (dict(d=256), -2), (dict(d=128, dtype=1), -2),
+    (dict(d=96), -2), (dict(d=512), -2), (dict(d=8), -2), (dict(d=128, dtype=1), -2),
+    (dict(d=256, dtype=1), -2),
 ])
 def test_rejected_sizes(kw, status):
     assert _check(**kw) == status
@@ -124,9 +127,65 @@ def test_status_strings():
 
 def test_tile_shape():
     assert aj.attn_jvp_tile_shape(0, 128) == (128, 64)
-    assert aj.attn_jvp_tile_shape(1, 64) == (128, 64)
+    assert aj.attn_jvp_tile_shape(0, 64) == (128, 64)
+    assert aj.attn_jvp_tile_shape(1, 64) == (64, 64)     # float32: four waves
     with pytest.raises(aj.AttnJvpError):
         aj.attn_jvp_tile_shape(1, 128)
+
+
+def test_tile_shape_unequal_head_dims():
+    # eight waves x 16 rows while the resident registers fit two waves per
+    # SIMD, else four; 64-key tiles while two LDS stages fit in 128 KiB
+    assert aj.attn_jvp_tile_shape_ex(0, 128, 128) == (128, 64)
+    assert aj.attn_jvp_tile_shape_ex(0, 256, 256) == (64, 32)
+    assert aj.attn_jvp_tile_shape_ex(0, 256, 64) == (128, 32)
+    assert aj.attn_jvp_tile_shape_ex(0, 64, 256) == (64, 32)
+    assert aj.attn_jvp_tile_shape_ex(0, 16, 128) == (128, 64)
+    assert aj.attn_jvp_tile_shape_ex(1, 16, 64) == (128, 64)
+    assert aj.attn_jvp_tile_shape(0, 128) == aj.attn_jvp_tile_shape_ex(0, 128, 128)
+    for args in ((0, 96, 64), (0, 64, 512), (1, 64, 128), (2, 64, 64)):
+        with pytest.raises(aj.AttnJvpError):
+            aj.attn_jvp_tile_shape_ex(*args)
+
+
+def _check_ex(B=1, H=2, Nq=100, Nkv=300, dqk=64, dv=128, dtype=0, lay=None, mask=None,
+              ptrs=None):
+    esize = 2 if dtype == 0 else 4
+    p = _ptrs(B, H, max(Nq, Nkv), max(dqk, dv), esize) if ptrs is None else ptrs
+    return aj.attn_jvp_check_ex(*p, aj.Shape(B, H, Nq, Nkv, dqk, dv), dtype, lay, mask)
+
+
+def test_check_ex_unequal_shapes():
+    assert _check_ex() == 0
+    assert _check_ex(Nq=300, Nkv=77, dqk=256, dv=16) == 0
+    assert _check_ex(dqk=32, dv=64, dtype=1) == 0
+    assert _check_ex(Nkv=0) == -1
+    assert _check_ex(dqk=48) == -2
+    assert _check_ex(dv=128, dtype=1) == -2
+    # the frame window is a self-attention mask with one head dim
+    fw = dict(frames=3, tokens_per_frame=100, chunk_frames=1, radius_chunks=0)
+    assert _check_ex(Nq=300, Nkv=300, dqk=64, dv=64, mask=fw) == 0
+    assert _check_ex(Nq=300, Nkv=300, dqk=64, dv=128, mask=fw) == -2
+    assert _check_ex(Nq=100, Nkv=300, dqk=64, dv=64, mask=fw) == -4
+
+
+def test_check_ex_extents_use_each_tensors_shape():
+    # contiguous layouts of the general shape; O directly after V must pass,
+    # O one row earlier overlaps V's last row
+    B, H, Nq, Nkv, dqk, dv = 1, 2, 40, 96, 32, 128
+    sizes = [B * H * n * d * 2 for n, d in ((Nq, dqk), (Nkv, dqk), (Nkv, dv),
+                                             (Nq, dqk), (Nkv, dqk), (Nkv, dv),
+                                             (Nq, dv), (Nq, dv))]
+    base, p = 1 << 40, []
+    for sz in sizes:
+        p.append(base)
+        base += sz
+    p += [base, base + B * H * Nq * 4]
+    shape = aj.Shape(B, H, Nq, Nkv, dqk, dv)
+    assert aj.attn_jvp_check_ex(*p, shape, 0, None, None) == 0
+    p2 = list(p)
+    p2[6] -= dv * 2
+    assert aj.attn_jvp_check_ex(*p2, shape, 0, None, None) == -3
 
 
 def _tiles_with_visible_pairs(w, N, bm, bn):

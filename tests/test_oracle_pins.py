@@ -44,6 +44,19 @@ def test_forward_matches_torch_sdpa(B, H, N, d, Nk):
     np.testing.assert_allclose(lse, torch.logsumexp(s, -1).numpy(), rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("N,Nk,d,dv", [(9, 23, 16, 48), (40, 7, 32, 8), (1, 5, 4, 1)])
+def test_forward_unequal_shapes_matches_torch_sdpa(N, Nk, d, dv):
+    # cross-attention shapes: Lq != Lkv and d_v != d_qk (the pages' op contract)
+    rng = np.random.default_rng(11)
+    q, k, v, dq, dk, dv_ = _rand(rng, 2, 2, N, d, Nk=Nk, dv=dv)
+    o, _, lse, _ = attention_jvp(q, k, v, dq, dk, dv_)
+    assert o.shape == (2, 2, N, dv) and lse.shape == (2, 2, N)
+    ref = torch.nn.functional.scaled_dot_product_attention(_t(q), _t(k), _t(v))
+    np.testing.assert_allclose(o, ref.numpy(), rtol=0, atol=1e-12)
+    s = _t(q) @ _t(k).transpose(-1, -2) * d ** -0.5
+    np.testing.assert_allclose(lse, torch.logsumexp(s, -1).numpy(), rtol=0, atol=1e-12)
+
+
 def test_forward_custom_scale_and_mask_matches_sdpa():
     rng = np.random.default_rng(2)
     q, k, v, dq, dk, dv = _rand(rng, 1, 2, 21, 6)
