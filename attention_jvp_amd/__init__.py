@@ -18,8 +18,9 @@ __all__ = [
     "ATTN_JVP_BF16", "ATTN_JVP_FP32", "AttnJvpError", "Layout", "Mask", "Shape",
     "attn_jvp_check", "attn_jvp_check_ex", "attn_jvp_fwd", "attn_jvp_fwd_ex",
     "attn_jvp_fwd_strided", "attn_jvp_status_string", "attn_jvp_tile_shape",
-    "attn_jvp_tile_shape_ex", "attn_jvp_visible_tiles", "exported_symbols", "fwd",
-    "library_path", "load",
+    "attn_jvp_tile_shape_ex", "attn_jvp_visible_tiles", "attn_jvp_fwd_partial",
+    "attn_jvp_merge", "attn_jvp_splitkv_plan", "attn_jvp_fwd_splitkv", "exported_symbols",
+    "fwd", "fwd_partial", "fwd_splitkv", "merge", "library_path", "load",
 ]
 
 ATTN_JVP_BF16 = 0
@@ -62,7 +63,8 @@ _lib = None
 
 EXPORTS = ("attn_jvp_fwd", "attn_jvp_fwd_strided", "attn_jvp_fwd_ex", "attn_jvp_check",
            "attn_jvp_check_ex", "attn_jvp_tile_shape", "attn_jvp_tile_shape_ex",
-           "attn_jvp_visible_tiles", "attn_jvp_status_string")
+           "attn_jvp_visible_tiles", "attn_jvp_fwd_partial", "attn_jvp_merge",
+           "attn_jvp_splitkv_plan", "attn_jvp_fwd_splitkv", "attn_jvp_status_string")
 
 
 def library_path():
@@ -96,6 +98,19 @@ def load():
     lib.attn_jvp_check_ex.restype = i32
     lib.attn_jvp_tile_shape_ex.argtypes = [i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.attn_jvp_tile_shape_ex.restype = i32
+    lib.attn_jvp_fwd_partial.argtypes = ptrs10 + [ctypes.POINTER(Shape), f32, i32,
+                                                  ctypes.POINTER(Layout), vp]
+    lib.attn_jvp_fwd_partial.restype = i32
+    lib.attn_jvp_merge.argtypes = [i32] + [vp] * 8 + [i32] * 5 + [i64p, vp]
+    lib.attn_jvp_merge.restype = i32
+    sz = ctypes.c_size_t
+    lib.attn_jvp_splitkv_plan.argtypes = [ctypes.POINTER(Shape), i32, ctypes.POINTER(Mask),
+                                          ctypes.POINTER(i32), ctypes.POINTER(sz)]
+    lib.attn_jvp_splitkv_plan.restype = i32
+    lib.attn_jvp_fwd_splitkv.argtypes = ptrs10 + [ctypes.POINTER(Shape), f32, i32,
+                                                  ctypes.POINTER(Layout), ctypes.POINTER(Mask),
+                                                  i32, vp, sz, vp]
+    lib.attn_jvp_fwd_splitkv.restype = i32
     lib.attn_jvp_tile_shape.argtypes = [i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.attn_jvp_tile_shape.restype = i32
     lib.attn_jvp_visible_tiles.argtypes = [i32, i32, i32, ctypes.POINTER(Mask), i64p]
@@ -154,6 +169,38 @@ def attn_jvp_check_ex(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, shape, dtype, layou
     lay = None if layout is None else ctypes.byref(layout)
     return load().attn_jvp_check_ex(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE,
                                     ctypes.byref(shape), dtype, lay, _mask_ptr(mask))
+
+
+def attn_jvp_fwd_partial(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, shape, scale, dtype,
+                         layout=None, stream=None):
+    lay = None if layout is None else ctypes.byref(layout)
+    return load().attn_jvp_fwd_partial(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE,
+                                       ctypes.byref(shape), scale, dtype, lay, stream)
+
+
+def attn_jvp_merge(num_parts, O_parts, dO_parts, LSE_parts, dLSE_parts, O, dO, LSE, dLSE,
+                   B, H, Lq, d_v, dtype, o_strides=None, stream=None):
+    st = None if o_strides is None else (ctypes.c_int64 * 3)(*o_strides)
+    return load().attn_jvp_merge(num_parts, O_parts, dO_parts, LSE_parts, dLSE_parts, O, dO,
+                                 LSE, dLSE, B, H, Lq, d_v, dtype, st, stream)
+
+
+def attn_jvp_splitkv_plan(shape, dtype, mask=None, num_splits=0):
+    """(num_splits used, workspace bytes) for a split-KV call."""
+    ns, ws = ctypes.c_int(num_splits), ctypes.c_size_t()
+    st = load().attn_jvp_splitkv_plan(ctypes.byref(shape), dtype, _mask_ptr(mask),
+                                      ctypes.byref(ns), ctypes.byref(ws))
+    if st != 0:
+        raise AttnJvpError(st, "attn_jvp_splitkv_plan")
+    return ns.value, ws.value
+
+
+def attn_jvp_fwd_splitkv(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, shape, scale, dtype, layout,
+                         mask, num_splits, workspace, workspace_bytes, stream=None):
+    lay = None if layout is None else ctypes.byref(layout)
+    return load().attn_jvp_fwd_splitkv(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE,
+                                       ctypes.byref(shape), scale, dtype, lay, _mask_ptr(mask),
+                                       num_splits, workspace, workspace_bytes, stream)
 
 
 def attn_jvp_tile_shape_ex(dtype, d_qk, d_v):
@@ -245,3 +292,104 @@ def fwd(q, k, v, dq, dk, dv, scale=None, mask=None, out=None):
     if st != 0:
         raise AttnJvpError(st, "attn_jvp_fwd_ex")
     return o, do, lse, dlse
+
+
+def _check_qkv(q, k, v, dq, dk, dv):
+    import torch
+    dtypes = {torch.bfloat16: ATTN_JVP_BF16, torch.float32: ATTN_JVP_FP32}
+    if q.dtype not in dtypes:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-d [B, H, L, d]")
+    B, H, Lq, dqk = q.shape
+    Lkv, dv_ = k.shape[2], v.shape[3]
+    if tuple(k.shape) != (B, H, Lkv, dqk) or tuple(v.shape) != (B, H, Lkv, dv_):
+        raise ValueError("shapes must be q [B,H,Lq,d_qk], k [B,H,Lkv,d_qk], v [B,H,Lkv,d_v]")
+    for t, ref in ((dq, q), (dk, k), (dv, v)):
+        if t.shape != ref.shape:
+            raise ValueError("each tangent must have its primal's shape")
+    for t in (k, v, dq, dk, dv):
+        if t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v, dq, dk, dv must share dtype and device")
+    return dtypes[q.dtype], Shape(B, H, Lq, Lkv, dqk, dv_)
+
+
+def fwd_partial(q, k, v, dq, dk, dv, scale=None):
+    """float32 partials (o, do, lse, dlse) of the keys given (see
+    attn_jvp_fwd_partial): o, do [B, H, Lq, d_v], lse, dlse [B, H, Lq]."""
+    import torch
+    dt, shape = _check_qkv(q, k, v, dq, dk, dv)
+    B, H, Lq, dv_ = shape.batch, shape.heads, shape.seqlen_q, shape.head_dim_v
+    o = torch.empty((B, H, Lq, dv_), device=q.device, dtype=torch.float32)
+    do = torch.empty_like(o)
+    lse = torch.empty((B, H, Lq), device=q.device, dtype=torch.float32)
+    dlse = torch.empty_like(lse)
+    lay = layout_of(q, k, v, dq, dk, dv, q, dq)     # o / dout strides are ignored
+    st = attn_jvp_fwd_partial(q.data_ptr(), k.data_ptr(), v.data_ptr(), dq.data_ptr(),
+                              dk.data_ptr(), dv.data_ptr(), o.data_ptr(), do.data_ptr(),
+                              lse.data_ptr(), dlse.data_ptr(), shape,
+                              0.0 if scale is None else float(scale), dt, lay,
+                              torch.cuda.current_stream(q.device).cuda_stream)
+    if st != 0:
+        raise AttnJvpError(st, "attn_jvp_fwd_partial")
+    return o, do, lse, dlse
+
+
+def merge(o_parts, do_parts, lse_parts, dlse_parts, dtype, out=None):
+    """Merge float32 partials stacked on a leading parts axis (o_parts, do_parts
+    [P, B, H, Lq, d_v], lse_parts, dlse_parts [P, B, H, Lq], contiguous) into
+    (o, do, lse, dlse) with o, do in ``dtype`` (torch.bfloat16/float32)."""
+    import torch
+    P, B, H, Lq, dv_ = o_parts.shape
+    for t in (o_parts, do_parts, lse_parts, dlse_parts):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("partials must be contiguous float32")
+    if tuple(do_parts.shape) != tuple(o_parts.shape) or tuple(lse_parts.shape) != (P, B, H, Lq) \
+            or tuple(dlse_parts.shape) != (P, B, H, Lq):
+        raise ValueError("inconsistent partial shapes")
+    dt = {torch.bfloat16: ATTN_JVP_BF16, torch.float32: ATTN_JVP_FP32}[dtype]
+    if out is None:
+        o = torch.empty((B, H, Lq, dv_), device=o_parts.device, dtype=dtype)
+        do = torch.empty_like(o)
+        lse = torch.empty((B, H, Lq), device=o_parts.device, dtype=torch.float32)
+        dlse = torch.empty_like(lse)
+    else:
+        o, do, lse, dlse = out
+    st = attn_jvp_merge(P, o_parts.data_ptr(), do_parts.data_ptr(), lse_parts.data_ptr(),
+                        dlse_parts.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                        dlse.data_ptr(), B, H, Lq, dv_, dt, _strides3(o),
+                        torch.cuda.current_stream(o_parts.device).cuda_stream)
+    if st != 0:
+        raise AttnJvpError(st, "attn_jvp_merge")
+    return o, do, lse, dlse
+
+
+def fwd_splitkv(q, k, v, dq, dk, dv, scale=None, mask=None, num_splits=0, workspace=None,
+                out=None):
+    """``fwd`` with key splits and a merge (attn_jvp_fwd_splitkv).  The
+    workspace (a CUDA uint8 tensor of at least the plan's size) is allocated
+    with torch.empty when not given.  Returns (o, do, lse, dlse, splits)."""
+    import torch
+    dt, shape = _check_qkv(q, k, v, dq, dk, dv)
+    ns, need = attn_jvp_splitkv_plan(shape, dt, mask, num_splits)
+    B, H, Lq, dv_ = shape.batch, shape.heads, shape.seqlen_q, shape.head_dim_v
+    if out is None:
+        o = torch.empty((B, H, Lq, dv_), device=q.device, dtype=q.dtype)
+        do = torch.empty_like(o)
+        lse = torch.empty((B, H, Lq), device=q.device, dtype=torch.float32)
+        dlse = torch.empty_like(lse)
+    else:
+        o, do, lse, dlse = out
+    if workspace is None and need:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    wp = 0 if workspace is None else workspace.data_ptr()
+    wb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lay = layout_of(q, k, v, dq, dk, dv, o, do)
+    st = attn_jvp_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), dq.data_ptr(),
+                              dk.data_ptr(), dv.data_ptr(), o.data_ptr(), do.data_ptr(),
+                              lse.data_ptr(), dlse.data_ptr(), shape,
+                              0.0 if scale is None else float(scale), dt, lay, mask, ns,
+                              wp or None, wb, torch.cuda.current_stream(q.device).cuda_stream)
+    if st != 0:
+        raise AttnJvpError(st, "attn_jvp_fwd_splitkv")
+    return o, do, lse, dlse, ns

@@ -127,10 +127,12 @@ attn_jvp_layout contiguous(const attn_jvp_shape &s) {
   return L;
 }
 
+// out_esize: bytes per O / dO element (the dtype's, or 4 for float32
+// partials); the o / dout strides of L are in those elements.
 int check_args(const void *Q, const void *K, const void *V, const void *dQ,
                const void *dK, const void *dV, void *O, void *dO, float *LSE,
                float *dLSE, const attn_jvp_shape *shape, int dtype,
-               const attn_jvp_layout *L, const attn_jvp_mask *mask) {
+               const attn_jvp_layout *L, const attn_jvp_mask *mask, int out_esize = 0) {
   if (!Q || !K || !V || !dQ || !dK || !dV || !O || !dO || !LSE || !dLSE || !shape || !L)
     return ATTN_JVP_EINVAL;
   const int B = shape->batch, H = shape->heads, Nq = shape->seqlen_q, Nkv = shape->seqlen_kv;
@@ -145,11 +147,13 @@ int check_args(const void *Q, const void *K, const void *V, const void *dQ,
       !same3(L->o, L->dout))
     return ATTN_JVP_ESTRIDE;
   const int esize = dtype == ATTN_JVP_BF16 ? 2 : 4;
-  const int64_t align = 16 / esize;
+  const int oes = out_esize ? out_esize : esize;
   const int64_t *all[4] = {L->q, L->k, L->v, L->o};
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    const int64_t align = 16 / (i == 3 ? oes : esize);
     for (int j = 0; j < 3; ++j)
       if (all[i][j] < 0 || all[i][j] % align != 0) return ATTN_JVP_ESTRIDE;
+  }
   // key-tile offsets use 24-bit row strides (in bytes)
   if (L->k[2] * esize >= (1 << 24) || L->v[2] * esize >= (1 << 24)) return ATTN_JVP_ESTRIDE;
   const void *ptrs[8] = {Q, K, V, dQ, dK, dV, O, dO};
@@ -162,8 +166,8 @@ int check_args(const void *Q, const void *K, const void *V, const void *dQ,
       extent_of(V, L->v, B, H, Nkv, dv, esize),   extent_of(dQ, L->q, B, H, Nq, dqk, esize),
       extent_of(dK, L->k, B, H, Nkv, dqk, esize), extent_of(dV, L->v, B, H, Nkv, dv, esize)};
   const int64_t rows = (int64_t)B * H * Nq;
-  const Extent out[4] = {extent_of(O, L->o, B, H, Nq, dv, esize),
-                         extent_of(dO, L->o, B, H, Nq, dv, esize),
+  const Extent out[4] = {extent_of(O, L->o, B, H, Nq, dv, oes),
+                         extent_of(dO, L->o, B, H, Nq, dv, oes),
                          Extent{(uintptr_t)LSE, (uintptr_t)LSE + (uintptr_t)(rows * 4)},
                          Extent{(uintptr_t)dLSE, (uintptr_t)dLSE + (uintptr_t)(rows * 4)}};
   for (int i = 0; i < 4; ++i) {
@@ -185,6 +189,89 @@ hipError_t dispatch(const Params &p, int dtype, int dqk, int dv, bool masked, hi
     case 256: return attn_jvp::launch_bf16_qk256(p, dv, masked, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+Params make_params(const void *Q, const void *K, const void *V, const void *dQ,
+                   const void *dK, const void *dV, void *O, void *dO, float *LSE,
+                   float *dLSE, const attn_jvp_shape &shape, float scale, int dtype,
+                   const attn_jvp_layout &L, const attn_jvp_mask *mask) {
+  Shape sh;
+  attn_jvp::shape_for(dtype == ATTN_JVP_BF16, shape.head_dim_qk, shape.head_dim_v, &sh);
+  Params p;
+  memset(&p, 0, sizeof(p));
+  p.q = Q; p.k = K; p.v = V; p.dq = dQ; p.dk = dK; p.dv = dV;
+  p.o = O; p.dout = dO; p.lse = LSE; p.dlse = dLSE;
+  for (int i = 0; i < 3; ++i) {
+    p.sq[i] = L.q[i];
+    p.sk[i] = L.k[i];
+    p.sv[i] = L.v[i];
+    p.so[i] = L.o[i];
+  }
+  p.B = shape.batch;
+  p.H = shape.heads;
+  p.Nq = shape.seqlen_q;
+  p.Nkv = shape.seqlen_kv;
+  p.nqb = (p.Nq + sh.block_m - 1) / sh.block_m;
+  p.nsplit = 1;
+  p.partial = 0;
+  p.scale = (scale > 0.f && isfinite(scale)) ? scale : 1.0f / sqrtf((float)shape.head_dim_qk);
+  p.scale_log2 = p.scale * 1.4426950408889634f;
+  p.mask = to_dev(mask);
+  return p;
+}
+
+// float32 partial outputs of a call: contiguous [B, H, Lq, d_v] in floats
+void partial_out_strides(const attn_jvp_shape &s, attn_jvp_layout *L) {
+  const int64_t o[3] = {(int64_t)s.heads * s.seqlen_q * s.head_dim_v,
+                        (int64_t)s.seqlen_q * s.head_dim_v, (int64_t)s.head_dim_v};
+  for (int i = 0; i < 3; ++i) L->o[i] = L->dout[i] = o[i];
+}
+
+// Split-KV workspace: O, dO partials [ns, B, H, Lq, d_v] then LSE, dLSE
+// partials [ns, B, H, Lq], float32, each region 256-byte aligned.
+struct SplitWs {
+  size_t o, dout, lse, dlse, total;
+};
+
+SplitWs split_workspace(const attn_jvp_shape &s, int ns) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t rows = (size_t)ns * s.batch * s.heads * s.seqlen_q;
+  SplitWs w;
+  w.o = 0;
+  w.dout = up(rows * s.head_dim_v * 4);
+  w.lse = w.dout + up(rows * s.head_dim_v * 4);
+  w.dlse = w.lse + up(rows * 4);
+  w.total = w.dlse + up(rows * 4);
+  return w;
+}
+
+// Key splits for one call: enough workgroups to fill the chip about four
+// times over, each split keeping at least two key tiles, at most 64.
+int choose_splits(const attn_jvp_shape &s, int dtype, const attn_jvp_mask *mask) {
+  Shape sh;
+  if (!attn_jvp::shape_for(dtype == ATTN_JVP_BF16, s.head_dim_qk, s.head_dim_v, &sh)) return 1;
+  const int64_t nqb = (s.seqlen_q + sh.block_m - 1) / sh.block_m;
+  const int64_t wgs = (int64_t)s.batch * s.heads * nqb;
+  int64_t tiles = (s.seqlen_kv + sh.block_n - 1) / sh.block_n;
+  if (mask_on(mask) && check_mask(mask, s.seqlen_q, s.seqlen_kv) == ATTN_JVP_OK) {
+    const MaskDev m = to_dev(mask);
+    int64_t mx = 0;
+    for (int64_t qb = 0; qb < nqb; ++qb) {
+      const int q0 = (int)(qb * sh.block_m);
+      const int q1 = q0 + sh.block_m < s.seqlen_q ? q0 + sh.block_m : s.seqlen_q;
+      const attn_jvp::TileRanges tr = attn_jvp::visible_tiles(m, q0, q1, s.seqlen_kv, sh.block_n);
+      int64_t c = 0;
+      for (int i = 0; i < tr.n; ++i) c += tr.hi[i] - tr.lo[i];
+      mx = c > mx ? c : mx;
+    }
+    tiles = mx;
+  }
+  const int64_t target = 4 * 256;
+  if (wgs >= target / 2) return 1;
+  int64_t ns = (target + wgs - 1) / wgs;
+  const int64_t cap = tiles / 2 > 1 ? tiles / 2 : 1;
+  ns = ns < cap ? ns : cap;
+  return (int)(ns < 64 ? ns : 64);
 }
 
 attn_jvp_shape square(int B, int H, int N, int d) {
@@ -218,28 +305,144 @@ int attn_jvp_fwd_ex(const void *Q, const void *K, const void *V, const void *dQ,
   const attn_jvp_layout L = layout ? *layout : contiguous(*shape);
   const int st = check_args(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, shape, dtype, &L, mask);
   if (st != ATTN_JVP_OK) return st;
-  Shape sh;
-  attn_jvp::shape_for(dtype == ATTN_JVP_BF16, shape->head_dim_qk, shape->head_dim_v, &sh);
-  Params p;
-  memset(&p, 0, sizeof(p));
-  p.q = Q; p.k = K; p.v = V; p.dq = dQ; p.dk = dK; p.dv = dV;
-  p.o = O; p.dout = dO; p.lse = LSE; p.dlse = dLSE;
-  for (int i = 0; i < 3; ++i) {
-    p.sq[i] = L.q[i];
-    p.sk[i] = L.k[i];
-    p.sv[i] = L.v[i];
-    p.so[i] = L.o[i];
-  }
-  p.B = shape->batch;
-  p.H = shape->heads;
-  p.Nq = shape->seqlen_q;
-  p.Nkv = shape->seqlen_kv;
-  p.nqb = (p.Nq + sh.block_m - 1) / sh.block_m;
-  p.scale = (scale > 0.f && isfinite(scale)) ? scale : 1.0f / sqrtf((float)shape->head_dim_qk);
-  p.scale_log2 = p.scale * 1.4426950408889634f;
-  p.mask = to_dev(mask);
+  const Params p = make_params(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, *shape, scale, dtype, L,
+                               mask);
   const hipError_t err = dispatch(p, dtype, shape->head_dim_qk, shape->head_dim_v,
                                   mask_on(mask), (hipStream_t)stream);
+  return err == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_EHIP;
+}
+
+int attn_jvp_fwd_partial(const void *Q, const void *K, const void *V, const void *dQ,
+                         const void *dK, const void *dV, float *O, float *dO, float *LSE,
+                         float *dLSE, const attn_jvp_shape *shape, float scale, int dtype,
+                         const attn_jvp_layout *layout, void *stream) {
+  if (!shape) return ATTN_JVP_EINVAL;
+  attn_jvp_layout L = layout ? *layout : contiguous(*shape);
+  partial_out_strides(*shape, &L);
+  const int st = check_args(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, shape, dtype, &L, nullptr, 4);
+  if (st != ATTN_JVP_OK) return st;
+  Params p = make_params(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, *shape, scale, dtype, L, nullptr);
+  p.partial = 1;
+  const hipError_t err = dispatch(p, dtype, shape->head_dim_qk, shape->head_dim_v, false,
+                                  (hipStream_t)stream);
+  return err == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_EHIP;
+}
+
+int attn_jvp_merge(int num_parts, const float *O_parts, const float *dO_parts,
+                   const float *LSE_parts, const float *dLSE_parts, void *O, void *dO,
+                   float *LSE, float *dLSE, int B, int H, int Lq, int d_v, int dtype,
+                   const int64_t *o_strides, void *stream) {
+  if (!O_parts || !dO_parts || !LSE_parts || !dLSE_parts || !O || !dO || !LSE || !dLSE)
+    return ATTN_JVP_EINVAL;
+  if (num_parts < 1 || B <= 0 || H <= 0 || Lq <= 0 || d_v <= 0) return ATTN_JVP_EINVAL;
+  if (dtype != ATTN_JVP_BF16 && dtype != ATTN_JVP_FP32) return ATTN_JVP_EINVAL;
+  if (d_v % 4 != 0) return ATTN_JVP_EUNSUPPORTED;
+  const int esize = dtype == ATTN_JVP_BF16 ? 2 : 4;
+  const int64_t rows = (int64_t)B * H * Lq;
+  if (rows * (d_v / 4) / 256 > 0x7fffffffLL) return ATTN_JVP_EINVAL;
+  const int64_t so[3] = {o_strides ? o_strides[0] : (int64_t)H * Lq * d_v,
+                         o_strides ? o_strides[1] : (int64_t)Lq * d_v,
+                         o_strides ? o_strides[2] : (int64_t)d_v};
+  for (int j = 0; j < 3; ++j)
+    if (so[j] < 0 || so[j] % 4 != 0) return ATTN_JVP_ESTRIDE;   // 4-wide stores
+  if ((uintptr_t)O_parts % 16 || (uintptr_t)dO_parts % 16 || (uintptr_t)O % (4 * esize) ||
+      (uintptr_t)dO % (4 * esize) || (uintptr_t)LSE_parts % 4 || (uintptr_t)dLSE_parts % 4 ||
+      (uintptr_t)LSE % 4 || (uintptr_t)dLSE % 4)
+    return ATTN_JVP_ESTRIDE;
+  const uintptr_t pe = (uintptr_t)(num_parts * rows * d_v * 4);
+  const uintptr_t le = (uintptr_t)(num_parts * rows * 4);
+  const Extent in[4] = {{(uintptr_t)O_parts, (uintptr_t)O_parts + pe},
+                        {(uintptr_t)dO_parts, (uintptr_t)dO_parts + pe},
+                        {(uintptr_t)LSE_parts, (uintptr_t)LSE_parts + le},
+                        {(uintptr_t)dLSE_parts, (uintptr_t)dLSE_parts + le}};
+  const Extent out[4] = {extent_of(O, so, B, H, Lq, d_v, esize),
+                         extent_of(dO, so, B, H, Lq, d_v, esize),
+                         {(uintptr_t)LSE, (uintptr_t)LSE + (uintptr_t)(rows * 4)},
+                         {(uintptr_t)dLSE, (uintptr_t)dLSE + (uintptr_t)(rows * 4)}};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 4; ++j)
+      if (overlaps(out[i], in[j])) return ATTN_JVP_ESTRIDE;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(out[i], out[j])) return ATTN_JVP_ESTRIDE;
+  }
+  attn_jvp::MergeParams m;
+  m.o_parts = O_parts; m.do_parts = dO_parts; m.lse_parts = LSE_parts; m.dlse_parts = dLSE_parts;
+  m.o = O; m.dout = dO; m.lse = LSE; m.dlse = dLSE;
+  for (int j = 0; j < 3; ++j) m.so[j] = so[j];
+  m.parts = num_parts; m.B = B; m.H = H; m.Nq = Lq; m.dv = d_v;
+  const hipError_t err = attn_jvp::launch_merge(m, dtype == ATTN_JVP_BF16, (hipStream_t)stream);
+  return err == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_EHIP;
+}
+
+int attn_jvp_splitkv_plan(const attn_jvp_shape *shape, int dtype, const attn_jvp_mask *mask,
+                          int *num_splits, size_t *workspace_bytes) {
+  if (!shape || !num_splits || !workspace_bytes) return ATTN_JVP_EINVAL;
+  if (shape->batch <= 0 || shape->heads <= 0 || shape->seqlen_q <= 0 || shape->seqlen_kv <= 0)
+    return ATTN_JVP_EINVAL;
+  if (dtype != ATTN_JVP_BF16 && dtype != ATTN_JVP_FP32) return ATTN_JVP_EINVAL;
+  Shape sh;
+  if (!attn_jvp::shape_for(dtype == ATTN_JVP_BF16, shape->head_dim_qk, shape->head_dim_v, &sh))
+    return ATTN_JVP_EUNSUPPORTED;
+  if (*num_splits < 0 || *num_splits > 1024) return ATTN_JVP_EINVAL;
+  const int ns = *num_splits ? *num_splits : choose_splits(*shape, dtype, mask);
+  *num_splits = ns;
+  *workspace_bytes = ns > 1 ? split_workspace(*shape, ns).total : 0;
+  return ATTN_JVP_OK;
+}
+
+int attn_jvp_fwd_splitkv(const void *Q, const void *K, const void *V, const void *dQ,
+                         const void *dK, const void *dV, void *O, void *dO, float *LSE,
+                         float *dLSE, const attn_jvp_shape *shape, float scale, int dtype,
+                         const attn_jvp_layout *layout, const attn_jvp_mask *mask,
+                         int num_splits, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+  if (!shape) return ATTN_JVP_EINVAL;
+  int ns = num_splits;
+  size_t need = 0;
+  int st = attn_jvp_splitkv_plan(shape, dtype, mask, &ns, &need);
+  if (st != ATTN_JVP_OK) return st;
+  if (ns == 1)
+    return attn_jvp_fwd_ex(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, shape, scale, dtype, layout,
+                           mask, stream);
+  const attn_jvp_layout L = layout ? *layout : contiguous(*shape);
+  st = check_args(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, shape, dtype, &L, mask);
+  if (st != ATTN_JVP_OK) return st;
+  if (!workspace || (uintptr_t)workspace % 256 != 0) return ATTN_JVP_EINVAL;
+  if (workspace_bytes < need) return ATTN_JVP_EINVAL;
+  Shape sh;
+  attn_jvp::shape_for(dtype == ATTN_JVP_BF16, shape->head_dim_qk, shape->head_dim_v, &sh);
+  const int64_t nqb = (shape->seqlen_q + sh.block_m - 1) / sh.block_m;
+  if ((int64_t)shape->batch * shape->heads * nqb * ns > 0x7fffffffLL) return ATTN_JVP_EINVAL;
+  // the workspace must not overlap the call's tensors
+  const Extent ws{(uintptr_t)workspace, (uintptr_t)workspace + need};
+  const int esize = dtype == ATTN_JVP_BF16 ? 2 : 4;
+  const int B = shape->batch, H = shape->heads, Nq = shape->seqlen_q, Nkv = shape->seqlen_kv;
+  const int dqk = shape->head_dim_qk, dv = shape->head_dim_v;
+  const Extent all[10] = {
+      extent_of(Q, L.q, B, H, Nq, dqk, esize),   extent_of(K, L.k, B, H, Nkv, dqk, esize),
+      extent_of(V, L.v, B, H, Nkv, dv, esize),   extent_of(dQ, L.q, B, H, Nq, dqk, esize),
+      extent_of(dK, L.k, B, H, Nkv, dqk, esize), extent_of(dV, L.v, B, H, Nkv, dv, esize),
+      extent_of(O, L.o, B, H, Nq, dv, esize),    extent_of(dO, L.o, B, H, Nq, dv, esize),
+      {(uintptr_t)LSE, (uintptr_t)LSE + (uintptr_t)((int64_t)B * H * Nq * 4)},
+      {(uintptr_t)dLSE, (uintptr_t)dLSE + (uintptr_t)((int64_t)B * H * Nq * 4)}};
+  for (int i = 0; i < 10; ++i)
+    if (overlaps(ws, all[i])) return ATTN_JVP_ESTRIDE;
+
+  const SplitWs w = split_workspace(*shape, ns);
+  char *base = (char *)workspace;
+  float *op = (float *)(base + w.o), *dop = (float *)(base + w.dout);
+  float *lp = (float *)(base + w.lse), *dlp = (float *)(base + w.dlse);
+  Params p = make_params(Q, K, V, dQ, dK, dV, op, dop, lp, dlp, *shape, scale, dtype, L, mask);
+  p.partial = 1;
+  p.nsplit = ns;
+  hipError_t err = dispatch(p, dtype, dqk, dv, mask_on(mask), (hipStream_t)stream);
+  if (err != hipSuccess) return ATTN_JVP_EHIP;
+  attn_jvp::MergeParams m;
+  m.o_parts = op; m.do_parts = dop; m.lse_parts = lp; m.dlse_parts = dlp;
+  m.o = O; m.dout = dO; m.lse = LSE; m.dlse = dLSE;
+  for (int j = 0; j < 3; ++j) m.so[j] = L.o[j];
+  m.parts = ns; m.B = B; m.H = H; m.Nq = Nq; m.dv = dv;
+  err = attn_jvp::launch_merge(m, dtype == ATTN_JVP_BF16, (hipStream_t)stream);
   return err == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_EHIP;
 }
 

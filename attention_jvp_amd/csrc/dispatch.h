@@ -22,4 +22,17 @@ hipError_t launch_fp32(const Params &p, int dqk, int dv, bool masked, hipStream_
 // Block shape of (bf16?, d_qk, d_v); false if the shape is not built.
 bool shape_for(bool bf16, int dqk, int dv, Shape *out);
 
+// Merge of key-split partials (merge.hip).  Partials are float32,
+// contiguous: O, dO [parts, B, H, Nq, dv], LSE, dLSE [parts, B, H, Nq].
+// Outputs: O, dO in the dtype with (b, h, n) element strides so[], LSE and
+// dLSE float32 contiguous [B, H, Nq].
+struct MergeParams {
+  const float *o_parts, *do_parts, *lse_parts, *dlse_parts;
+  void *o, *dout;
+  float *lse, *dlse;
+  int64_t so[3];
+  int parts, B, H, Nq, dv;
+};
+hipError_t launch_merge(const MergeParams &m, bool bf16, hipStream_t s);
+
 }  // namespace attn_jvp

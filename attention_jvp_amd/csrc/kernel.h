@@ -208,6 +208,8 @@ struct Params {
   int64_t sq[3], sk[3], sv[3], so[3];   // (b, h, n) element strides
   int B, H, Nq, Nkv;
   int nqb;                              // query blocks per (b, h)
+  int nsplit;                           // key splits per query block (1: none)
+  int partial;                          // 1: outputs are float32 partials
   float scale, scale_log2;
   MaskDev mask;
 };
@@ -431,7 +433,10 @@ __global__ __launch_bounds__((Cfg<T, DQK, DV>::kThreads), 1) void attn_jvp_kerne
   const int qi = lane & 15;        // this lane's query within the wave
   const int lg = lane >> 4;        // lane group 0..3
 
-  const int lid = logical_block_id();
+  // logical id = (bh * nqb + qb) * nsplit + split
+  const int lid_all = logical_block_id();
+  const int lid = lid_all / p.nsplit;
+  const int split = lid_all - lid * p.nsplit;
   const int bh = lid / p.nqb;
   const int qb = lid - bh * p.nqb;
   const int b = bh / p.H;
@@ -453,8 +458,13 @@ __global__ __launch_bounds__((Cfg<T, DQK, DV>::kThreads), 1) void attn_jvp_kerne
     tr.hi[0] = (Nkv + BN - 1) / BN;
     tr.lo[1] = tr.hi[1] = tr.lo[2] = tr.hi[2] = 0;
   }
-  // unused ranges are empty (lo = hi = 0)
-  const int ntile = (tr.hi[0] - tr.lo[0]) + (tr.hi[1] - tr.lo[1]) + (tr.hi[2] - tr.lo[2]);
+  // unused ranges are empty (lo = hi = 0).  With key splits, this workgroup
+  // takes the split-th run of ceil(n / nsplit) of the n visited tiles.
+  const int nvis = (tr.hi[0] - tr.lo[0]) + (tr.hi[1] - tr.lo[1]) + (tr.hi[2] - tr.lo[2]);
+  const int per_split = (nvis + p.nsplit - 1) / p.nsplit;
+  const int t_first = split * per_split;
+  const int t_last = t_first + per_split < nvis ? t_first + per_split : nvis;
+  const int ntile = t_last > t_first ? t_last - t_first : 0;
 
   // first tile in flight before anything else
   SideCopier<T, RBK, BN, W, true> kcopy;
@@ -464,7 +474,7 @@ __global__ __launch_bounds__((Cfg<T, DQK, DV>::kThreads), 1) void attn_jvp_kerne
   vcopy.init((const T *)p.v + b * p.sv[0] + h * p.sv[1],
              (const T *)p.dv + b * p.sv[0] + h * p.sv[1], p.sv[2], wave, lane);
   auto issue_tile = [&](int it, int g) __attribute__((always_inline)) {
-    const int k0 = tile_at(tr, it) * BN;
+    const int k0 = tile_at(tr, t_first + it) * BN;
     kcopy.issue(k0, Nkv, smem + g * TK, 2 * TK);
     vcopy.issue(k0, Nkv, smem + VB + g * TV, 2 * TV);
   };
@@ -733,7 +743,7 @@ __global__ __launch_bounds__((Cfg<T, DQK, DV>::kThreads), 1) void attn_jvp_kerne
   auto tile = [&](auto G_, int it) __attribute__((always_inline)) {
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
-    const int k0 = tile_at(tr, it) * BN;
+    const int k0 = tile_at(tr, t_first + it) * BN;
     const bool need = needs_mask(k0);
     wait_vmem();
     __syncthreads();   // tile `it` landed; every wave is done with tile it-1
@@ -780,7 +790,29 @@ __global__ __launch_bounds__((Cfg<T, DQK, DV>::kThreads), 1) void attn_jvp_kerne
   const float inv = empty ? 0.f : 1.f / l_tot;
   const float mu = scale * row_sum4(r_run) * inv;   // dLSE
   const float sinv = scale * inv;
-  if (qvalid) {
+  if (qvalid && p.partial) {
+    // float32 partial of this key split: O, dO [split, B, H, Lq, d_v] and
+    // LSE, dLSE [split, B, H, Lq], contiguous
+    const int64_t row = ((int64_t)split * p.B * p.H + bh) * Nq + qrow;
+    float *O = (float *)p.o + row * DV;
+    float *dO = (float *)p.dout + row * DV;
+#pragma unroll
+    for (int e = 0; e < ND; ++e) {
+      const int d0 = 16 * e + 4 * lg;
+      f32x4 ov, dv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ov[i] = oacc[e][i] * inv;
+        dv[i] = fmaf(bacc[e][i], sinv, aacc[e][i] * inv) - mu * ov[i];
+      }
+      *(f32x4 *)(O + d0) = ov;
+      *(f32x4 *)(dO + d0) = dv;
+    }
+    if (lg == 0) {
+      p.lse[row] = empty ? -INFINITY : (m_run + log2f(l_tot)) * 0.69314718055994530942f;
+      p.dlse[row] = mu;
+    }
+  } else if (qvalid) {
     T *O = (T *)p.o + b * p.so[0] + h * p.so[1] + (int64_t)qrow * p.so[2];
     T *dO = (T *)p.dout + b * p.so[0] + h * p.so[1] + (int64_t)qrow * p.so[2];
     // each lane owns 4 consecutive d of its row per d block: one packed
@@ -807,11 +839,11 @@ __global__ __launch_bounds__((Cfg<T, DQK, DV>::kThreads), 1) void attn_jvp_kerne
   }
 }
 
-// Launch one instance: grid = B * H * ceil(Nq / block_m) workgroups.
+// Launch one instance: grid = B * H * ceil(Nq / block_m) * nsplit workgroups.
 template <typename T, int DQK, int DV, bool MASKED>
 hipError_t launch_instance(const Params &p, hipStream_t stream) {
   using C = Cfg<T, DQK, DV>;
-  const int grid = p.B * p.H * p.nqb;
+  const int grid = p.B * p.H * p.nqb * p.nsplit;
   hipLaunchKernelGGL((attn_jvp_kernel<T, DQK, DV, MASKED>), dim3(grid), dim3(C::kThreads), 0,
                      stream, p);
   return hipGetLastError();

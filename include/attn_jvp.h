@@ -24,8 +24,9 @@
  * chunks on each side, first/last frames as always-visible anchor keys.
  *
  * Conventions shared by every entry point:
- *   - Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE are DEVICE pointers owned by the
- *     caller; the library allocates and frees no device memory.
+ *   - Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE (and split partials and
+ *     workspaces) are DEVICE pointers owned by the caller; the library
+ *     allocates and frees no device memory.
  *   - Shapes follow the pages' op contract: Q, dQ are [B, H, Lq, d_qk];
  *     K, dK are [B, H, Lkv, d_qk]; V, dV are [B, H, Lkv, d_v]; O, dO are
  *     [B, H, Lq, d_v]; LSE, dLSE are [B, H, Lq].  The square entry points
@@ -50,6 +51,7 @@
 #ifndef ATTN_JVP_H
 #define ATTN_JVP_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -134,6 +136,68 @@ int attn_jvp_check_ex(const void *Q, const void *K, const void *V,
                       void *O, void *dO, float *LSE, float *dLSE,
                       const attn_jvp_shape *shape, int dtype,
                       const attn_jvp_layout *layout, const attn_jvp_mask *mask);
+
+/* ---- Key splits -------------------------------------------------------
+ * Attention over a union of disjoint key sets combines from per-set results:
+ * with (O_k, dO_k, LSE_k, dLSE_k) of set k over the same query rows,
+ *   LSE  = log sum_k exp(LSE_k),   w_k = exp(LSE_k - LSE),
+ *   O    = sum_k w_k O_k,          dLSE = sum_k w_k dLSE_k,
+ *   dO   = sum_k w_k (dO_k + (dLSE_k - dLSE) O_k).
+ * (Derived from the definition above; the pages do not state it.)  This is
+ * what lets one query block's keys be split over several workgroups, or a
+ * long sequence's keys over several calls (ring-style context parallelism),
+ * and it is why dLSE is an output.
+ *
+ * Float32 partials of key set k are laid out contiguous: O_parts and
+ * dO_parts [num_parts, B, H, Lq, d_v], LSE_parts and dLSE_parts
+ * [num_parts, B, H, Lq].  A row that sees no key of a set has LSE_k = -inf,
+ * dLSE_k = 0 and O_k = dO_k = 0. */
+
+/* attn_jvp_fwd_ex restricted to the keys it is given (pass K, dK, V, dV
+ * already offset to a key range and Lkv = its length), writing float32
+ * partials O, dO [B, H, Lq, d_v] and LSE, dLSE [B, H, Lq], contiguous (the
+ * o / dout strides of `layout` are ignored).  No mask.  Returns a status. */
+int attn_jvp_fwd_partial(const void *Q, const void *K, const void *V,
+                         const void *dQ, const void *dK, const void *dV,
+                         float *O, float *dO, float *LSE, float *dLSE,
+                         const attn_jvp_shape *shape, float scale, int dtype,
+                         const attn_jvp_layout *layout, void *stream);
+
+/* Merge num_parts float32 partials (layout above) into O, dO (the dtype,
+ * [B, H, Lq, d_v] with element strides o_strides[3] = (b, h, row), NULL =
+ * contiguous; strides multiples of 4) and LSE, dLSE (float32, contiguous
+ * [B, H, Lq]).  d_v must be a multiple of 4.  Outputs must not overlap the
+ * partials.  Asynchronous on `stream`.  Returns a status. */
+int attn_jvp_merge(int num_parts, const float *O_parts, const float *dO_parts,
+                   const float *LSE_parts, const float *dLSE_parts,
+                   void *O, void *dO, float *LSE, float *dLSE,
+                   int B, int H, int Lq, int d_v, int dtype,
+                   const int64_t *o_strides, void *stream);
+
+/* Host-only: the key splits attn_jvp_fwd_splitkv uses for a call and the
+ * device workspace it needs.  *num_splits: in, the requested count (0 =
+ * choose: enough workgroups to fill the chip about four times, each split
+ * keeping at least two key tiles, at most 64); out, the count used.
+ * *workspace_bytes is 0 when one split is used.  Returns a status. */
+int attn_jvp_splitkv_plan(const attn_jvp_shape *shape, int dtype,
+                          const attn_jvp_mask *mask, int *num_splits,
+                          size_t *workspace_bytes);
+
+/* attn_jvp_fwd_ex with each query block's visited key tiles divided over
+ * num_splits workgroups (0 = the plan's choice): the splits write float32
+ * partials into `workspace` (device memory owned by the caller, 256-byte
+ * aligned, at least the plan's workspace_bytes, not overlapping any tensor),
+ * then a merge kernel writes O, dO, LSE, dLSE.  Both launches go to
+ * `stream`; the workspace is free again once they complete.  With one
+ * split this is attn_jvp_fwd_ex and the workspace is unused (may be NULL).
+ * For few query blocks and long key sequences.  Returns a status. */
+int attn_jvp_fwd_splitkv(const void *Q, const void *K, const void *V,
+                         const void *dQ, const void *dK, const void *dV,
+                         void *O, void *dO, float *LSE, float *dLSE,
+                         const attn_jvp_shape *shape, float scale, int dtype,
+                         const attn_jvp_layout *layout,
+                         const attn_jvp_mask *mask, int num_splits,
+                         void *workspace, size_t workspace_bytes, void *stream);
 
 /* Contiguous [B, H, N, d] tensors.  scale <= 0 selects 1/sqrt(d).
  * Returns an attn_jvp_status. */

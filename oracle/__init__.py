@@ -16,12 +16,15 @@ Sources (the page "带分数正则的一致性蒸馏", gitcode.csdn.net, section
   "VDN-Minimax-H3 ... Stage A1" (yfxerp.com), used by the long-video workload.
 * ``trigflow``       -- the TrigFlow <-> rectified-flow coefficients of the
   section 时间步转换 of the first page.
+* ``merge``          -- the combination of results over disjoint key sets
+  (derived from the definition; not on the pages).
 
 Every function is pinned by the ``-m "not gpu"`` tests in ``tests/``.
 """
 
 from .attention_jvp import attention_jvp, attention_jvp_rows
 from .masks import FrameWindow, frame_window_visible
+from .merge import merge_partials
 from .streaming import attention_jvp_streaming
 from . import trigflow
 
@@ -31,5 +34,6 @@ __all__ = [
     "attention_jvp_streaming",
     "FrameWindow",
     "frame_window_visible",
+    "merge_partials",
     "trigflow",
 ]

@@ -117,10 +117,8 @@ def make_inputs(w, seed=None):
     B, H, N, d = w.B, w.H, w.N, w.d
     rows = {"q": N, "k": w.Nkv, "v": w.Nkv}
     cols = {"q": d, "k": d, "v": w.dv}
-    out = {}
-    for n in ("q", "k", "v"):
-        out[n] = torch.empty((B, H, rows[n], cols[n]), dtype=tdt)
-        out["d" + n] = torch.empty((B, H, rows[n], cols[n]), dtype=tdt)
+    out = {n: torch.empty((B, H, rows[n[-1]], cols[n[-1]]), dtype=tdt)
+           for n in ("q", "k", "v", "dq", "dk", "dv")}
 
     if w.tangents == "trigflow":
         if w.Nkv != N or w.dv != d:

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 from oracle import (FrameWindow, attention_jvp, attention_jvp_rows,
-                    attention_jvp_streaming)
+                    attention_jvp_streaming, merge_partials)
 
 
 def _rand(rng, B, H, N, d, Nk=None, dv=None, scale_t=1.0):
@@ -209,21 +209,47 @@ def test_streaming_recurrence_matches_dense_masked():
 
 
 def test_split_kv_merge_identity():
-    # Outputs over two disjoint key sets merge into the full result:
-    # LSE = logaddexp(LSE1, LSE2), w_i = exp(LSE_i - LSE), O = sum w_i O_i,
-    # dLSE = sum w_i dLSE_i, dO = sum w_i (dO_i + (dLSE_i - dLSE) O_i).
+    # results over two disjoint key sets merge into the full result computed
+    # directly from the definition
     rng = np.random.default_rng(13)
     q, k, v, dq, dk, dv = _rand(rng, 1, 2, 11, 8, Nk=30)
     full = attention_jvp(q, k, v, dq, dk, dv)
     sl = [slice(0, 13), slice(13, 30)]
     parts = [attention_jvp(q, k[:, :, s], v[:, :, s], dq, dk[:, :, s], dv[:, :, s]) for s in sl]
-    lse = np.logaddexp(parts[0][2], parts[1][2])
-    wts = [np.exp(p[2] - lse) for p in parts]
-    o = sum(w[..., None] * p[0] for w, p in zip(wts, parts))
-    dlse = sum(w * p[3] for w, p in zip(wts, parts))
-    do = sum(w[..., None] * (p[1] + (p[3] - dlse)[..., None] * p[0]) for w, p in zip(wts, parts))
-    for a, b in zip(full, (o, do, lse, dlse)):
+    for a, b in zip(full, merge_partials(parts)):
         np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+
+
+def test_merge_with_empty_parts_and_empty_rows():
+    # a frame window split into key ranges: some rows see no key of a range
+    # (LSE_k = -inf there); rows of a query frame cut off from every key
+    # (a window with no anchors over a key subset) stay empty after the merge
+    rng = np.random.default_rng(17)
+    N = 24
+    q, k, v, dq, dk, dv = _rand(rng, 1, 2, N, 6, dv=5)
+    w = FrameWindow(frames=8, tokens_per_frame=3, chunk_frames=2, radius_chunks=0,
+                    anchor_first=True, anchor_last=False)
+    full = attention_jvp(q, k, v, dq, dk, dv, visible=w)
+    cuts = [0, 5, 6, 17, 24]
+    parts = []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        vis = (lambda a_: (lambda qi, ki: w(qi, ki + a_)))(a)
+        parts.append(attention_jvp(q, k[:, :, a:b], v[:, :, a:b], dq, dk[:, :, a:b],
+                                   dv[:, :, a:b], visible=vis))
+    assert any(np.isneginf(p[2]).any() for p in parts)
+    merged = merge_partials(parts)
+    for a, b in zip(full, merged):
+        np.testing.assert_array_equal(np.isfinite(a), np.isfinite(b))
+        fin = np.isfinite(a)
+        np.testing.assert_allclose(a[fin], b[fin], rtol=0, atol=1e-12)
+    # keys 12..23 only: query frames 0..1 (chunk 0) see nothing there
+    sub = attention_jvp(q, k[:, :, 12:], v[:, :, 12:], dq, dk[:, :, 12:], dv[:, :, 12:],
+                        visible=lambda qi, ki: w(qi, ki + 12))
+    o, do, lse, dlse = merge_partials([sub, sub])
+    rows = np.arange(6)
+    assert np.isneginf(lse[:, :, rows]).all()
+    assert (o[:, :, rows] == 0).all() and (do[:, :, rows] == 0).all()
+    assert (dlse[:, :, rows] == 0).all()
 
 
 def test_invisible_keys_do_not_matter():
