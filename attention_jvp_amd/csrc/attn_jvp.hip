@@ -245,8 +245,9 @@ SplitWs split_workspace(const attn_jvp_shape &s, int ns) {
   return w;
 }
 
-// Key splits for one call: enough workgroups to fill the chip about four
-// times over, each split keeping at least two key tiles, at most 64.
+// Key splits for one call: enough workgroups to fill the chip about twice
+// over (more splits only add partial traffic for the merge), each split
+// keeping at least two key tiles, at most 64.
 int choose_splits(const attn_jvp_shape &s, int dtype, const attn_jvp_mask *mask) {
   Shape sh;
   if (!attn_jvp::shape_for(dtype == ATTN_JVP_BF16, s.head_dim_qk, s.head_dim_v, &sh)) return 1;
@@ -266,7 +267,7 @@ int choose_splits(const attn_jvp_shape &s, int dtype, const attn_jvp_mask *mask)
     }
     tiles = mx;
   }
-  const int64_t target = 4 * 256;
+  const int64_t target = 2 * 256;
   if (wgs >= target / 2) return 1;
   int64_t ns = (target + wgs - 1) / wgs;
   const int64_t cap = tiles / 2 > 1 ? tiles / 2 : 1;

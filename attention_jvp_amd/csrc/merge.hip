@@ -12,7 +12,7 @@
 // identity itself follows from the definition and is not on the pages.
 //
 // Memory-bound: each thread owns 4 consecutive d_v columns of one row and
-// reads 2 * num_parts float4 values plus the row's per-part scalars.
+// reads 2 * num_parts float4 values plus the row's per-part scalars, once.
 
 #include <hip/hip_runtime.h>
 
@@ -36,14 +36,52 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams m) {
   const int n = (int)(row - bh * m.Nq);
   const int b = (int)(bh / m.H), h = (int)(bh - (int64_t)b * m.H);
 
-  // row scalars: LSE, dLSE
-  // IEEE maximum: a NaN in any part propagates to the row, as in one pass
-  float mx = -INFINITY;
-  for (int k = 0; k < m.parts; ++k)
-    mx = __builtin_elementwise_maximum(mx, m.lse_parts[k * rows + row]);
   T *O = (T *)m.o + b * m.so[0] + h * m.so[1] + (int64_t)n * m.so[2] + c;
   T *dO = (T *)m.dout + b * m.so[0] + h * m.so[1] + (int64_t)n * m.so[2] + c;
   typedef T T4 __attribute__((ext_vector_type(4)));
+  typedef float f4 __attribute__((ext_vector_type(4)));
+
+  // One pass over the parts with a running maximum mx (online log-sum-exp):
+  // with u_k = exp(LSE_k - mx), accumulate su = sum u_k, sd = sum u_k dLSE_k,
+  // ob = sum u_k O_k and ub = sum u_k (dO_k + dLSE_k O_k).  Then w_k = u_k/su,
+  // and dO = sum w_k (dO_k + dLSE_k O_k) - dLSE O, the identity above with
+  // the dLSE term taken out of the sum.
+  float mx = -INFINITY, su = 0.f, sd = 0.f;
+  f4 ob = {0.f, 0.f, 0.f, 0.f}, ub = {0.f, 0.f, 0.f, 0.f};
+  auto fold = [&](float lk, float dk, f4 ok, f4 gk) {
+    // IEEE maximum: a NaN in any part propagates to the row, as in one pass
+    const float mn = __builtin_elementwise_maximum(mx, lk);
+    if (mn == -INFINITY) return;                      // nothing seen yet
+    const float alpha = expf(mx - mn);                // 0 on the first seen part
+    const float u = expf(lk - mn);                    // 0 for an empty part
+    su = su * alpha + u;
+    sd = sd * alpha + u * dk;
+    ob = ob * alpha + u * ok;
+    ub = ub * alpha + u * (gk + dk * ok);
+    mx = mn;
+  };
+  // four parts' loads in flight before they are folded in order
+  constexpr int G = 4;
+  int k = 0;
+  for (; k + G <= m.parts; k += G) {
+    float lk[G], dk[G];
+    f4 ok[G], gk[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int64_t r = (int64_t)(k + j) * rows + row;
+      lk[j] = m.lse_parts[r];
+      dk[j] = m.dlse_parts[r];
+      ok[j] = *(const f4 *)(m.o_parts + r * m.dv + c);
+      gk[j] = *(const f4 *)(m.do_parts + r * m.dv + c);
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) fold(lk[j], dk[j], ok[j], gk[j]);
+  }
+  for (; k < m.parts; ++k) {
+    const int64_t r = (int64_t)k * rows + row;
+    fold(m.lse_parts[r], m.dlse_parts[r], *(const f4 *)(m.o_parts + r * m.dv + c),
+         *(const f4 *)(m.do_parts + r * m.dv + c));
+  }
   if (mx == -INFINITY) {                 // no part saw a key: the empty-row convention
     T4 z;
     for (int i = 0; i < 4; ++i) z[i] = (T)0.f;
@@ -55,37 +93,18 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams m) {
     }
     return;
   }
-  float sum = 0.f;
-  for (int k = 0; k < m.parts; ++k) sum += expf(m.lse_parts[k * rows + row] - mx);
-  const float lse = mx + logf(sum);
-  float dlse = 0.f;
-  for (int k = 0; k < m.parts; ++k) {
-    const float w = expf(m.lse_parts[k * rows + row] - lse);
-    dlse += w * m.dlse_parts[k * rows + row];
-  }
-
-  // columns c..c+3
-  typedef float f4 __attribute__((ext_vector_type(4)));
-  f4 o = {0.f, 0.f, 0.f, 0.f}, d = {0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < m.parts; ++k) {
-    const float lk = m.lse_parts[k * rows + row];
-    const float w = expf(lk - lse);                      // 0 for an empty part
-    const float g = m.dlse_parts[k * rows + row] - dlse;
-    const int64_t off = (k * rows + row) * m.dv + c;
-    const f4 ok = *(const f4 *)(m.o_parts + off);
-    const f4 dk = *(const f4 *)(m.do_parts + off);
-    o += w * ok;                      // an empty part has w = 0, O_k = dO_k = 0
-    d += w * (dk + g * ok);
-  }
+  const float inv = 1.f / su;
+  const float dlse = sd * inv;
   T4 ov, dv;
   for (int i = 0; i < 4; ++i) {
-    ov[i] = (T)o[i];
-    dv[i] = (T)d[i];
+    const float o = ob[i] * inv;
+    ov[i] = (T)o;
+    dv[i] = (T)(ub[i] * inv - dlse * o);
   }
   *(T4 *)O = ov;
   *(T4 *)dO = dv;
   if (c == 0) {
-    m.lse[row] = lse;
+    m.lse[row] = mx + logf(su);
     m.dlse[row] = dlse;
   }
 }

@@ -4,9 +4,14 @@
 One step is one attn_jvp_fwd call over the whole workload with the inputs
 already resident in HBM.  The timed region is bracketed by device
 synchronisation and timed with HIP events recorded on the stream the kernel
-is launched on.  Counted FLOPs are 12 * (visible query-key pairs) * d per
-(batch, head): the six N^2 d products of the definition (QK^T, dQ K^T,
-Q dK^T, P V, P dV, (P . dS) V).
+is launched on.  Counted FLOPs are 6 * (visible query-key pairs) * (d_qk +
+d_v) per (batch, head): the six products of the definition (QK^T, dQ K^T,
+Q dK^T over d_qk; P V, P dV, (P . dS) V over d_v), 12 N^2 d when square.
+
+``--shape B,H,Lq,Lkv,d_qk,d_v`` times a synthetic shape instead of a named
+workload (Gaussian inputs, tangents x 0.1); ``--splitkv S`` times the
+split-KV path (attn_jvp_fwd_splitkv with S splits, 0 = the library's
+choice; the workspace is allocated once, outside the timed region).
 
 Prints one JSON line.  ``--gpus`` above 1 is refused: this path runs on one
 GPU.
@@ -55,10 +60,11 @@ def visible_pairs(N, mask):
 
 
 def kernel_sha():
-    """sha256 over the kernel sources (every file of csrc/, by name)."""
+    """sha256 over the sources of the attention kernel itself: the template
+    (kernel.h) and its instance units (inst.h, inst_*.hip), by name."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(KERNEL_SOURCES)):
-        if name.endswith((".hip", ".h")):
+        if name == "kernel.h" or name.startswith("inst"):
             h.update(name.encode())
             with open(os.path.join(KERNEL_SOURCES, name), "rb") as f:
                 h.update(f.read())
@@ -117,17 +123,17 @@ def cpu_baseline(w, x, target_s):
     nrows = int(max(16, min(w.N, (target_s - fixed) / per_row)))
     dt, rows = run(nrows)
     if vis is None:
-        pairs = len(rows) * w.N
+        pairs = len(rows) * w.Nkv
     else:
-        pairs = int(vis(rows, np.arange(w.N)).sum())
-    flops = 12.0 * w.B * w.H * pairs * w.d
+        pairs = int(vis(rows, np.arange(w.Nkv)).sum())
+    flops = 6.0 * w.B * w.H * pairs * (w.d + w.dv)
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": blas_threads(),
         "kind": "oracle",
         "sample": (f"{len(rows)} evenly spaced query rows x {w.B * w.H} heads of {w.name} "
-                   f"against all {w.N} keys, float64 numpy; {dt:.1f} s"),
+                   f"against all {w.Nkv} keys, float64 numpy; {dt:.1f} s"),
     }
 
 
@@ -137,6 +143,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="image_dit_4096")
+    ap.add_argument("--shape", default=None, metavar="B,H,Lq,Lkv,DQK,DV",
+                    help="time this synthetic shape instead of a named workload")
+    ap.add_argument("--splitkv", type=int, default=-1, metavar="S",
+                    help="time attn_jvp_fwd_splitkv with S key splits (0 = library choice)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target length of the timed oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -164,21 +174,36 @@ def main():
         return
 
     import attention_jvp_amd as aj
-    from synth import WORKLOADS, make_inputs
+    from synth import WORKLOADS, Workload, make_inputs
 
-    w = WORKLOADS[args.workload]
-    log(f"workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype}")
+    if args.shape:
+        B, H, Lq, Lkv, dqk, dv = (int(t) for t in args.shape.split(","))
+        w = Workload(f"shape_{B}x{H}x{Lq}x{Lkv}x{dqk}x{dv}", B, H, Lq, dqk, "bf16", 1,
+                     tangent_scale=0.1, n_kv=Lkv, d_v=dv)
+    else:
+        w = WORKLOADS[args.workload]
+    log(f"workload {w.name}: B={w.B} H={w.H} Lq={w.N} Lkv={w.Nkv} d_qk={w.d} d_v={w.dv} {w.dtype}")
     x = make_inputs(w)
     g = [x[n].cuda() for n in NAMES]
-    o = torch.empty_like(g[0])
+    o = torch.empty((w.B, w.H, w.N, w.dv), device="cuda", dtype=g[0].dtype)
     do = torch.empty_like(o)
     lse = torch.empty((w.B, w.H, w.N), device="cuda", dtype=torch.float32)
     dlse = torch.empty_like(lse)
     outs = (o, do, lse, dlse)
     mask = x["mask"]
+    splits = None
+    if args.splitkv >= 0:
+        dt = aj.ATTN_JVP_BF16 if w.dtype == "bf16" else aj.ATTN_JVP_FP32
+        splits, need = aj.attn_jvp_splitkv_plan(aj.Shape(w.B, w.H, w.N, w.Nkv, w.d, w.dv), dt,
+                                                mask, args.splitkv)
+        ws = torch.empty(max(need, 256), device="cuda", dtype=torch.uint8)
+        log(f"split-KV: {splits} splits, workspace {need} bytes")
 
     def step():
-        aj.fwd(*g, mask=mask, out=outs)
+        if splits is None:
+            aj.fwd(*g, mask=mask, out=outs)
+        else:
+            aj.fwd_splitkv(*g, mask=mask, num_splits=splits, workspace=ws, out=outs)
 
     for _ in range(args.warmup):
         step()
@@ -192,8 +217,8 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
-    pairs = visible_pairs(w.N, mask)
-    flops = 12.0 * w.B * w.H * pairs * w.d
+    pairs = visible_pairs(w.N, mask) if mask is not None else w.N * w.Nkv
+    flops = 6.0 * w.B * w.H * pairs * (w.d + w.dv)
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     log(f"{ms:.4f} ms/step, {tflops:.1f} TFLOP/s ({100 * tflops / peak:.1f}% of {peak} peak)")
@@ -220,6 +245,8 @@ def main():
         "pct_of_peak": round(100 * tflops / peak, 2),
         "config": {
             "workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+            **({"Lkv": w.Nkv, "d_v": w.dv} if (w.Nkv != w.N or w.dv != w.d) else {}),
+            **({"splitkv": splits} if splits is not None else {}),
             "mask": mask, "visible_pairs_per_head": pairs,
             "counted_flops": flops,
         },
@@ -229,7 +256,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(tflops / peak, 4),
-            "traffic": traffic_record(w.name),
+            "traffic": traffic_record(w.name) if splits is None else None,
         },
         "cpu_baseline": cpu,
     }

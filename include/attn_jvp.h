@@ -176,7 +176,7 @@ int attn_jvp_merge(int num_parts, const float *O_parts, const float *dO_parts,
 
 /* Host-only: the key splits attn_jvp_fwd_splitkv uses for a call and the
  * device workspace it needs.  *num_splits: in, the requested count (0 =
- * choose: enough workgroups to fill the chip about four times, each split
+ * choose: enough workgroups to fill the chip about twice, each split
  * keeping at least two key tiles, at most 64); out, the count used.
  * *workspace_bytes is 0 when one split is used.  Returns a status. */
 int attn_jvp_splitkv_plan(const attn_jvp_shape *shape, int dtype,
