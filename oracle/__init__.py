@@ -18,17 +18,21 @@ Sources (the page "带分数正则的一致性蒸馏", gitcode.csdn.net, section
   section 时间步转换 of the first page.
 * ``merge``          -- the combination of results over disjoint key sets
   (derived from the definition; not on the pages).
+* ``backward``       -- the primal gradients dQ, dK, dV from the saved
+  log-sum-exp (subsection 反向).
 
 Every function is pinned by the ``-m "not gpu"`` tests in ``tests/``.
 """
 
 from .attention_jvp import attention_jvp, attention_jvp_rows
+from .backward import attention_backward
 from .masks import FrameWindow, frame_window_visible
 from .merge import merge_partials
 from .streaming import attention_jvp_streaming
 from . import trigflow
 
 __all__ = [
+    "attention_backward",
     "attention_jvp",
     "attention_jvp_rows",
     "attention_jvp_streaming",
