@@ -21,6 +21,7 @@ __all__ = [
     "attn_jvp_tile_shape_ex", "attn_jvp_visible_tiles", "attn_jvp_fwd_partial",
     "attn_jvp_merge", "attn_jvp_splitkv_plan", "attn_jvp_fwd_splitkv", "exported_symbols",
     "fwd", "fwd_partial", "fwd_splitkv", "merge", "library_path", "load",
+    "BwdLayout", "attn_jvp_bwd", "attn_jvp_bwd_check", "bwd",
 ]
 
 ATTN_JVP_BF16 = 0
@@ -54,6 +55,10 @@ class Layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64 * 3) for n in ("q", "k", "v", "dq", "dk", "dv", "o", "dout")]
 
 
+class BwdLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64 * 3) for n in ("q", "k", "v", "o", "go", "gq", "gk", "gv")]
+
+
 class Shape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "heads", "seqlen_q", "seqlen_kv", "head_dim_qk", "head_dim_v")]
@@ -64,7 +69,8 @@ _lib = None
 EXPORTS = ("attn_jvp_fwd", "attn_jvp_fwd_strided", "attn_jvp_fwd_ex", "attn_jvp_check",
            "attn_jvp_check_ex", "attn_jvp_tile_shape", "attn_jvp_tile_shape_ex",
            "attn_jvp_visible_tiles", "attn_jvp_fwd_partial", "attn_jvp_merge",
-           "attn_jvp_splitkv_plan", "attn_jvp_fwd_splitkv", "attn_jvp_status_string")
+           "attn_jvp_splitkv_plan", "attn_jvp_fwd_splitkv", "attn_jvp_bwd",
+           "attn_jvp_bwd_check", "attn_jvp_status_string")
 
 
 def library_path():
@@ -111,6 +117,12 @@ def load():
                                                   ctypes.POINTER(Layout), ctypes.POINTER(Mask),
                                                   i32, vp, sz, vp]
     lib.attn_jvp_fwd_splitkv.restype = i32
+    lib.attn_jvp_bwd.argtypes = [vp] * 10 + [ctypes.POINTER(Shape), f32, i32,
+                                             ctypes.POINTER(BwdLayout), vp]
+    lib.attn_jvp_bwd.restype = i32
+    lib.attn_jvp_bwd_check.argtypes = [vp] * 10 + [ctypes.POINTER(Shape), i32,
+                                                   ctypes.POINTER(BwdLayout)]
+    lib.attn_jvp_bwd_check.restype = i32
     lib.attn_jvp_tile_shape.argtypes = [i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.attn_jvp_tile_shape.restype = i32
     lib.attn_jvp_visible_tiles.argtypes = [i32, i32, i32, ctypes.POINTER(Mask), i64p]
@@ -201,6 +213,19 @@ def attn_jvp_fwd_splitkv(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, shape, scale, dt
     return load().attn_jvp_fwd_splitkv(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE,
                                        ctypes.byref(shape), scale, dtype, lay, _mask_ptr(mask),
                                        num_splits, workspace, workspace_bytes, stream)
+
+
+def attn_jvp_bwd(Q, K, V, O, gO, LSE, gQ, gK, gV, delta, shape, scale, dtype, layout=None,
+                 stream=None):
+    lay = None if layout is None else ctypes.byref(layout)
+    return load().attn_jvp_bwd(Q, K, V, O, gO, LSE, gQ, gK, gV, delta, ctypes.byref(shape),
+                               scale, dtype, lay, stream)
+
+
+def attn_jvp_bwd_check(Q, K, V, O, gO, LSE, gQ, gK, gV, delta, shape, dtype, layout=None):
+    lay = None if layout is None else ctypes.byref(layout)
+    return load().attn_jvp_bwd_check(Q, K, V, O, gO, LSE, gQ, gK, gV, delta,
+                                     ctypes.byref(shape), dtype, lay)
 
 
 def attn_jvp_tile_shape_ex(dtype, d_qk, d_v):
@@ -393,3 +418,41 @@ def fwd_splitkv(q, k, v, dq, dk, dv, scale=None, mask=None, num_splits=0, worksp
     if st != 0:
         raise AttnJvpError(st, "attn_jvp_fwd_splitkv")
     return o, do, lse, dlse, ns
+
+
+def bwd(q, k, v, o, go, lse, scale=None, out=None):
+    """Primal gradients (gq, gk, gv, delta) of a loss with dL/dO = go, for
+    q [B, H, Lq, d], k, v [B, H, Lkv, d], o, go [B, H, Lq, d] (bf16 or
+    float32) and the forward's lse [B, H, Lq] (float32).  delta is
+    rowsum(go * o).  Outputs are allocated contiguous unless
+    ``out = (gq, gk, gv, delta)`` is given.  Runs on the current stream."""
+    import torch
+    dtypes = {torch.bfloat16: ATTN_JVP_BF16, torch.float32: ATTN_JVP_FP32}
+    if q.dtype not in dtypes:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    B, H, Lq, d = q.shape
+    Lkv = k.shape[2]
+    if tuple(k.shape) != (B, H, Lkv, d) or tuple(v.shape) != (B, H, Lkv, v.shape[3]) \
+            or tuple(o.shape) != (B, H, Lq, v.shape[3]) or go.shape != o.shape:
+        raise ValueError("shapes must be q [B,H,Lq,d], k, v [B,H,Lkv,d], o, go [B,H,Lq,d]")
+    if tuple(lse.shape) != (B, H, Lq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, Lq]")
+    for t in (k, v, o, go):
+        if t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v, o, go must share dtype and device")
+    if out is None:
+        gq, gk, gv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        delta = torch.empty((B, H, Lq), device=q.device, dtype=torch.float32)
+    else:
+        gq, gk, gv, delta = out
+    lay = BwdLayout()
+    for name, t in zip(("q", "k", "v", "o", "go", "gq", "gk", "gv"), (q, k, v, o, go, gq, gk, gv)):
+        getattr(lay, name)[:] = _strides3(t)
+    shape = Shape(B, H, Lq, Lkv, d, v.shape[3])
+    st = attn_jvp_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), go.data_ptr(),
+                      lse.data_ptr(), gq.data_ptr(), gk.data_ptr(), gv.data_ptr(),
+                      delta.data_ptr(), shape, 0.0 if scale is None else float(scale),
+                      dtypes[q.dtype], lay, torch.cuda.current_stream(q.device).cuda_stream)
+    if st != 0:
+        raise AttnJvpError(st, "attn_jvp_bwd")
+    return gq, gk, gv, delta

@@ -17,9 +17,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 UNITS = ["attn_jvp.hip", "inst_bf16_qk16.hip", "inst_bf16_qk32.hip", "inst_bf16_qk64.hip",
-         "inst_bf16_qk128.hip", "inst_bf16_qk256.hip", "inst_fp32.hip", "merge.hip"]
+         "inst_bf16_qk128.hip", "inst_bf16_qk256.hip", "inst_fp32.hip", "merge.hip",
+         "inst_bwd.hip"]
 SOURCES = [os.path.join(CSRC, u) for u in UNITS]
-HEADERS = [os.path.join(CSRC, h) for h in ("kernel.h", "dispatch.h", "inst.h")] + [
+HEADERS = [os.path.join(CSRC, h) for h in ("kernel.h", "dispatch.h", "inst.h", "bwd.h")] + [
     os.path.join(ROOT, "include", "attn_jvp.h")]
 OUTPUT = os.path.join(HERE, "libattn_jvp.so")
 

@@ -12,6 +12,7 @@
 #include <string.h>
 
 #include "attn_jvp.h"
+#include "bwd.h"
 #include "dispatch.h"
 
 namespace attn_jvp {
@@ -275,6 +276,68 @@ int choose_splits(const attn_jvp_shape &s, int dtype, const attn_jvp_mask *mask)
   return (int)(ns < 64 ? ns : 64);
 }
 
+attn_jvp_bwd_layout contiguous_bwd(const attn_jvp_shape &s) {
+  const attn_jvp_layout f = contiguous(s);
+  attn_jvp_bwd_layout L;
+  for (int i = 0; i < 3; ++i) {
+    L.q[i] = L.gq[i] = f.q[i];
+    L.k[i] = L.gk[i] = f.k[i];
+    L.v[i] = L.gv[i] = f.v[i];
+    L.o[i] = L.go[i] = f.o[i];
+  }
+  return L;
+}
+
+int check_bwd(const void *Q, const void *K, const void *V, const void *O, const void *gO,
+              const float *LSE, void *gQ, void *gK, void *gV, float *delta,
+              const attn_jvp_shape *shape, int dtype, const attn_jvp_bwd_layout *L) {
+  if (!Q || !K || !V || !O || !gO || !LSE || !gQ || !gK || !gV || !delta || !shape || !L)
+    return ATTN_JVP_EINVAL;
+  const int B = shape->batch, H = shape->heads, Nq = shape->seqlen_q, Nkv = shape->seqlen_kv;
+  const int d = shape->head_dim_qk;
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nkv <= 0 || d <= 0 || shape->head_dim_v <= 0)
+    return ATTN_JVP_EINVAL;
+  if (dtype != ATTN_JVP_BF16 && dtype != ATTN_JVP_FP32) return ATTN_JVP_EINVAL;
+  if (shape->head_dim_v != d) return ATTN_JVP_EUNSUPPORTED;   // the pages: one head dim
+  int bq, bk;
+  if (!attn_jvp::bwd_shape_for(dtype == ATTN_JVP_BF16, d, &bq, &bk)) return ATTN_JVP_EUNSUPPORTED;
+  if ((int64_t)B * H * ((Nq + bq - 1) / bq) > 0x7fffffffLL ||
+      (int64_t)B * H * ((Nkv + bk - 1) / bk) > 0x7fffffffLL)
+    return ATTN_JVP_EINVAL;
+  const int esize = dtype == ATTN_JVP_BF16 ? 2 : 4;
+  const int64_t align = 16 / esize;
+  const int64_t *all[8] = {L->q, L->k, L->v, L->o, L->go, L->gq, L->gk, L->gv};
+  for (int i = 0; i < 8; ++i)
+    for (int j = 0; j < 3; ++j)
+      if (all[i][j] < 0 || all[i][j] % align != 0) return ATTN_JVP_ESTRIDE;
+  // streamed tiles use 24-bit row strides (in bytes)
+  const int64_t *streamed[4] = {L->q, L->k, L->v, L->go};
+  for (int i = 0; i < 4; ++i)
+    if (streamed[i][2] * esize >= (1 << 24)) return ATTN_JVP_ESTRIDE;
+  const void *ptrs[8] = {Q, K, V, O, gO, gQ, gK, gV};
+  for (int i = 0; i < 8; ++i)
+    if ((uintptr_t)ptrs[i] % 16 != 0) return ATTN_JVP_ESTRIDE;
+  if ((uintptr_t)LSE % 4 != 0 || (uintptr_t)delta % 4 != 0) return ATTN_JVP_ESTRIDE;
+  const int64_t rows = (int64_t)B * H * Nq;
+  const Extent in[6] = {extent_of(Q, L->q, B, H, Nq, d, esize),
+                        extent_of(K, L->k, B, H, Nkv, d, esize),
+                        extent_of(V, L->v, B, H, Nkv, d, esize),
+                        extent_of(O, L->o, B, H, Nq, d, esize),
+                        extent_of(gO, L->go, B, H, Nq, d, esize),
+                        {(uintptr_t)LSE, (uintptr_t)LSE + (uintptr_t)(rows * 4)}};
+  const Extent out[4] = {extent_of(gQ, L->gq, B, H, Nq, d, esize),
+                         extent_of(gK, L->gk, B, H, Nkv, d, esize),
+                         extent_of(gV, L->gv, B, H, Nkv, d, esize),
+                         {(uintptr_t)delta, (uintptr_t)delta + (uintptr_t)(rows * 4)}};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(out[i], in[j])) return ATTN_JVP_ESTRIDE;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(out[i], out[j])) return ATTN_JVP_ESTRIDE;
+  }
+  return ATTN_JVP_OK;
+}
+
 attn_jvp_shape square(int B, int H, int N, int d) {
   attn_jvp_shape s;
   s.batch = B;
@@ -444,6 +507,46 @@ int attn_jvp_fwd_splitkv(const void *Q, const void *K, const void *V, const void
   for (int j = 0; j < 3; ++j) m.so[j] = L.o[j];
   m.parts = ns; m.B = B; m.H = H; m.Nq = Nq; m.dv = dv;
   err = attn_jvp::launch_merge(m, dtype == ATTN_JVP_BF16, (hipStream_t)stream);
+  return err == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_EHIP;
+}
+
+int attn_jvp_bwd_check(const void *Q, const void *K, const void *V, const void *O,
+                       const void *gO, const float *LSE, void *gQ, void *gK, void *gV,
+                       float *delta, const attn_jvp_shape *shape, int dtype,
+                       const attn_jvp_bwd_layout *layout) {
+  if (!shape) return ATTN_JVP_EINVAL;
+  const attn_jvp_bwd_layout L = layout ? *layout : contiguous_bwd(*shape);
+  return check_bwd(Q, K, V, O, gO, LSE, gQ, gK, gV, delta, shape, dtype, &L);
+}
+
+int attn_jvp_bwd(const void *Q, const void *K, const void *V, const void *O, const void *gO,
+                 const float *LSE, void *gQ, void *gK, void *gV, float *delta,
+                 const attn_jvp_shape *shape, float scale, int dtype,
+                 const attn_jvp_bwd_layout *layout, void *stream) {
+  if (!shape) return ATTN_JVP_EINVAL;
+  const attn_jvp_bwd_layout L = layout ? *layout : contiguous_bwd(*shape);
+  const int st = check_bwd(Q, K, V, O, gO, LSE, gQ, gK, gV, delta, shape, dtype, &L);
+  if (st != ATTN_JVP_OK) return st;
+  int bq, bk;
+  attn_jvp::bwd_shape_for(dtype == ATTN_JVP_BF16, shape->head_dim_qk, &bq, &bk);
+  attn_jvp::BwdParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = Q; p.k = K; p.v = V; p.o = O; p.g = gO; p.lse = LSE;
+  p.gq = gQ; p.gk = gK; p.gv = gV; p.delta = delta;
+  for (int i = 0; i < 3; ++i) {
+    p.sq[i] = L.q[i]; p.sk[i] = L.k[i]; p.sv[i] = L.v[i]; p.so[i] = L.o[i];
+    p.sg[i] = L.go[i]; p.sgq[i] = L.gq[i]; p.sgk[i] = L.gk[i]; p.sgv[i] = L.gv[i];
+  }
+  p.B = shape->batch;
+  p.H = shape->heads;
+  p.Nq = shape->seqlen_q;
+  p.Nkv = shape->seqlen_kv;
+  p.nqb = (p.Nq + bq - 1) / bq;
+  p.nkb = (p.Nkv + bk - 1) / bk;
+  p.scale = (scale > 0.f && isfinite(scale)) ? scale : 1.0f / sqrtf((float)shape->head_dim_qk);
+  p.scale_log2 = p.scale * 1.4426950408889634f;
+  const hipError_t err = attn_jvp::launch_bwd(p, dtype == ATTN_JVP_BF16, shape->head_dim_qk,
+                                              (hipStream_t)stream);
   return err == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_EHIP;
 }
 

@@ -1,0 +1,412 @@
+// Primal backward of attention for gfx950: dQ, dK, dV from the saved
+// log-sum-exp (page "带分数正则的一致性蒸馏", gitcode.csdn.net, section 注意力,
+// subsection 反向).  With the upstream gradient G = dL/dO:
+//   P = exp(s Q K^T - LSE),  dV = P^T G,  dP = G V^T,
+//   dS = P (.) (dP - D),  D = rowsum(dP (.) P) = rowsum(G (.) O),
+//   dQ = s dS K,  dK = s dS^T Q.
+// The pages parallelise dQ over query tokens and dK, dV over key tokens (two
+// tilings); so do these two kernels, with no atomics:
+//   * bwd_dq_kernel: a workgroup owns query rows (16 per wave; Q and G
+//     fragments in registers), streams K and V tiles through LDS, writes D
+//     (from its own rows of G and O) and dQ;
+//   * bwd_dkv_kernel: a workgroup owns key rows (16 per wave; K and V
+//     fragments in registers), streams Q and G tiles through LDS, reads D and
+//     LSE per query, writes dK and dV.
+// Both recompute S and P; MFMA fragment layouts, LDS staging (asynchronous
+// global->LDS copies, two stages, swizzled rows) and transposing reads are
+// those of the forward kernel (kernel.h).  d_qk = d_v = D, as the pages
+// require for the backward.
+
+#pragma once
+
+#include "kernel.h"
+
+namespace attn_jvp {
+
+struct BwdParams {
+  const void *q, *k, *v, *o, *g;   // inputs; g = dL/dO
+  const float *lse;                // [B, H, Nq], natural log, from the forward
+  void *gq, *gk, *gv;              // outputs dL/dQ, dL/dK, dL/dV
+  float *delta;                    // [B, H, Nq]: D = rowsum(G (.) O), written by the dQ kernel
+  int64_t sq[3], sk[3], sv[3], so[3], sg[3], sgq[3], sgk[3], sgv[3];   // (b, h, n) strides
+  int B, H, Nq, Nkv;
+  int nqb, nkb;                    // query / key blocks per (b, h)
+  float scale, scale_log2;
+};
+
+// Global->LDS copies of the streamed tiles: SideCopier's scheme (1 KiB per
+// wave instruction, lane-chosen swizzled chunk, clamped tail rows) for two
+// tensors with their own row strides.
+template <typename T, int RB, int BN, int W>
+struct PairCopier {
+  static constexpr int CPR = RB / 16;
+  static constexpr int TILE = BN * RB;
+  static constexpr int NI = TILE / 1024;
+  static constexpr int IPW = (NI + W - 1) / W;
+  static_assert(NI * 1024 == TILE, "a tile is whole 1 KiB wave copies");
+
+  const char *base[2];
+  int64_t rstride[2];
+  uint32_t rs[2];           // below 2^24 bytes, checked on the host
+  uint32_t slot[IPW];       // (row << 16) | swizzled chunk, per lane
+  int wave;
+
+  __device__ void init(const T *t0, const T *t1, int64_t s0, int64_t s1, int wave_, int lane) {
+    wave = wave_;
+    base[0] = (const char *)t0;
+    base[1] = (const char *)t1;
+    rstride[0] = s0 * (int64_t)sizeof(T);
+    rstride[1] = s1 * (int64_t)sizeof(T);
+    rs[0] = (uint32_t)rstride[0];
+    rs[1] = (uint32_t)rstride[1];
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int s = (i * W + wave) * 64 + lane;
+      const int r = s / CPR;
+      const int c = (s % CPR) ^ kswz<RB>(r);
+      slot[i] = ((uint32_t)r << 16) | (uint32_t)c;
+    }
+  }
+
+  __device__ void issue(int k0, int N, char *dst0, int tstride) const {
+    const int valid = (N - k0 < BN ? N - k0 : BN) - 1;   // last real row
+    const char *tb0 = base[0] + (int64_t)k0 * rstride[0];
+    const char *tb1 = base[1] + (int64_t)k0 * rstride[1];
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      if (NI % W != 0 && i * W + wave >= NI) break;   // uniform per wave
+      uint32_t r = slot[i] >> 16;
+      r = r < (uint32_t)valid ? r : (uint32_t)valid;
+      const uint32_t c16 = (slot[i] & 0xffffu) << 4;
+      char *dst = dst0 + (i * W + wave) * 1024;
+      __builtin_amdgcn_global_load_lds((const void *)(tb0 + __umul24(r, rs[0]) + c16),
+                                       (lds_void *)dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(tb1 + __umul24(r, rs[1]) + c16),
+                                       (lds_void *)(dst + tstride), 16, 0, 0);
+    }
+  }
+};
+
+template <typename T, int D>
+struct BwdCfg {
+  static constexpr int ES = (int)sizeof(T);
+  static constexpr int RB = D * ES;
+  // resident per lane: two operand fragment sets and one (dQ) or two (dK,
+  // dV) accumulator sets
+  static constexpr int kResDq = (ES == 2 ? D / 4 : D / 2) + D / 4;
+  static constexpr int kResDkv = (ES == 2 ? D / 4 : D / 2) + D / 2;
+  static constexpr int kWavesDq = kResDq <= 96 ? 8 : 4;
+  static constexpr int kWavesDkv = kResDkv <= 96 ? 8 : 4;
+  // 64-row tiles while two stages of both tensors fit in 128 KiB and the
+  // transposing reads' largest constant offset (stage, second tensor, row
+  // 48 of the tile) fits the 16-bit DS offset field; else 32
+  static constexpr int kBN = (4 * 64 * RB <= 128 * 1024 && 3 * 64 * RB + 48 * RB < 65536) ? 64 : 32;
+  static constexpr int kLds = 4 * kBN * RB;                         // 2 stages x 2 tensors
+};
+
+template <typename T, int D, bool KEYS>
+__global__ __launch_bounds__((64 * (KEYS ? BwdCfg<T, D>::kWavesDkv : BwdCfg<T, D>::kWavesDq)), 1)
+void bwd_kernel(BwdParams p) {
+  using C = BwdCfg<T, D>;
+  using EK = ElemK<T, D>;
+  using EV = ElemV<T>;
+  using FragK = typename EK::Frag;
+  using FragV = typename EV::Frag;
+  constexpr bool BF16 = sizeof(T) == 2;
+  constexpr int W = KEYS ? C::kWavesDkv : C::kWavesDq;
+  constexpr int BN = C::kBN;
+  constexpr int CK = kStepKeys;
+  constexpr int NSTEP = BN / CK;
+  constexpr int KL = EK::KL, KI = EK::KI;
+  constexpr int RB = C::RB;
+  constexpr int TL = BN * RB;          // bytes per tensor tile
+  constexpr int DS = D / KI;
+  constexpr int ND = D / 16;
+  constexpr float kLog2e = 1.4426950408889634f;
+
+  __shared__ __attribute__((aligned(1024))) char smem[C::kLds];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rl = lane & 15;       // this lane's owned row (query or key) within the wave
+  const int lg = lane >> 4;
+
+  const int lid = logical_block_id();
+  const int nblk = KEYS ? p.nkb : p.nqb;
+  const int bh = lid / nblk;
+  const int blk = lid - bh * nblk;
+  const int b = bh / p.H;
+  const int h = bh - b * p.H;
+  const int Nq = p.Nq, Nkv = p.Nkv;
+  const int Nown = KEYS ? Nkv : Nq;      // rows this kernel owns
+  const int Nstr = KEYS ? Nq : Nkv;      // rows it streams
+
+  // owned: (A, Bt) = (Q, G) for dQ, (K, V) for dK, dV -- B operands in registers
+  const T *A0 = KEYS ? (const T *)p.k + b * p.sk[0] + h * p.sk[1]
+                     : (const T *)p.q + b * p.sq[0] + h * p.sq[1];
+  const T *A1 = KEYS ? (const T *)p.v + b * p.sv[0] + h * p.sv[1]
+                     : (const T *)p.g + b * p.sg[0] + h * p.sg[1];
+  const int64_t as0 = KEYS ? p.sk[2] : p.sq[2];
+  const int64_t as1 = KEYS ? p.sv[2] : p.sg[2];
+  // streamed: tensor 0 (K for dQ, Q for dK/dV) and tensor 1 (V for dQ, G for dK/dV)
+  const T *S0 = KEYS ? (const T *)p.q + b * p.sq[0] + h * p.sq[1]
+                     : (const T *)p.k + b * p.sk[0] + h * p.sk[1];
+  const T *S1 = KEYS ? (const T *)p.g + b * p.sg[0] + h * p.sg[1]
+                     : (const T *)p.v + b * p.sv[0] + h * p.sv[1];
+  const int64_t ss0 = KEYS ? p.sq[2] : p.sk[2];
+  const int64_t ss1 = KEYS ? p.sg[2] : p.sv[2];
+  const float *LSE = p.lse + (int64_t)bh * Nq;
+  float *DEL = p.delta + (int64_t)bh * Nq;
+
+  const int r0 = blk * (W * kWaveRows);
+  const int row = r0 + wave * kWaveRows + rl;     // owned row of this lane
+  const bool rvalid = row < Nown;
+  const int ntile = (Nstr + BN - 1) / BN;
+
+  // streamed tiles: both tensors have rows of D elements, one copier; the
+  // same tile is read as operand rows and through transposing loads, so
+  // one swizzle (the operand-row rule) serves both
+  PairCopier<T, RB, BN, W> copier;
+  copier.init(S0, S1, ss0, ss1, wave, lane);
+  auto issue_tile = [&](int it, int g) __attribute__((always_inline)) {
+    copier.issue(it * BN, Nstr, smem + g * TL, 2 * TL);
+  };
+  issue_tile(0, 0);
+
+  // owned fragments (B operands): lane holds row rl, d-slice s KI + lg KL
+  FragK af[DS], bf[DS];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) {
+    if (rvalid) {
+      af[s] = *(const FragK *)(A0 + (int64_t)row * as0 + s * KI + lg * KL);
+      bf[s] = *(const FragK *)(A1 + (int64_t)row * as1 + s * KI + lg * KL);
+    } else {
+      af[s] = FragK{};
+      bf[s] = FragK{};
+    }
+  }
+
+  // dQ kernel: the lane's query row terms.  D = rowsum(G (.) O) from the
+  // lane's quarter of the row (the same d-slices as its G fragments),
+  // summed over the row's four lanes; L2 = LSE * log2 e (+inf for a row
+  // with no visible key, so that P = 0 there).
+  float d_row = 0.f, l2_row = 0.f;
+  if constexpr (!KEYS) {
+    const T *Orow = (const T *)p.o + b * p.so[0] + h * p.so[1];
+    float part = 0.f;
+    if (rvalid) {
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        const FragK of = *(const FragK *)(Orow + (int64_t)row * p.so[2] + s * KI + lg * KL);
+        if constexpr (BF16) {
+#pragma unroll
+          for (int j = 0; j < KL; ++j) part = fmaf((float)bf[s][j], (float)of[j], part);
+        } else {
+          part = fmaf(bf[s], of, part);
+        }
+      }
+    }
+    d_row = row_sum4(part);
+    if (rvalid && lg == 0) DEL[row] = d_row;
+    const float lse = rvalid ? LSE[row] : 0.f;
+    l2_row = lse == -INFINITY ? INFINITY : lse * kLog2e;
+  }
+
+  // accumulators: dQ^T (dQ kernel) or dK^T and dV^T (dK/dV kernel); lane
+  // holds d = 16e + 4 lg + 0..3 of its owned row
+  f32x4 acc0[ND], acc1[KEYS ? ND : 1];
+#pragma unroll
+  for (int e = 0; e < ND; ++e) acc0[e] = f32x4{};
+  if constexpr (KEYS) {
+#pragma unroll
+    for (int e = 0; e < ND; ++e) acc1[e] = f32x4{};
+  }
+
+  const float c2 = p.scale_log2;
+  const uint32_t smem_a = lds_addr(smem);
+  uint32_t rdl[DS];                          // operand-row reads, k-step s
+#pragma unroll
+  for (int s = 0; s < DS; ++s)
+    rdl[s] = smem_a + lds_off<RB, true>(rl, (s * KI + lg * KL) * (int)sizeof(T));
+  uint32_t trl[BF16 ? ND : 1];               // transposing reads, d block e
+  if constexpr (BF16) {
+#pragma unroll
+    for (int e = 0; e < ND; ++e)
+      trl[e] = smem_a + lds_off<RB, true>(4 * lg + (rl >> 2), (16 * e + 4 * (rl & 3)) * 2);
+  }
+
+  // One 32-row step kc of the streamed tile in stage G.
+  //  dQ kernel:   X^T = K Q^T (keys x queries), Y^T = V G^T; lane: query rl,
+  //               keys 4 lg + i (+16 for the second half)
+  //  dK/dV kernel: X = Q K^T (queries x keys), Y = G V^T; lane: key rl,
+  //               queries 4 lg + i (+16)
+  auto step = [&](auto G_, auto KC_, int t0) __attribute__((always_inline)) {
+    constexpr int G = decltype(G_)::value;
+    constexpr int kb = decltype(KC_)::value * CK;
+    f32x4 xs[2], ys[2];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      f32x4 x_ = f32x4{}, y_ = f32x4{};
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        const char *rp = smem + (rdl[s] - smem_a) + G * TL + (kb + 16 * kb2) * RB;
+        const FragK r0f = *(const FragK *)rp;
+        const FragK r1f = *(const FragK *)(rp + 2 * TL);
+        x_ = EK::mfma(r0f, af[s], x_);
+        y_ = EK::mfma(r1f, bf[s], y_);
+      }
+      xs[kb2] = x_;
+      ys[kb2] = y_;
+    }
+    // P and dS = P (.) (dP - D), unscaled; streamed rows past the end and
+    // (dK/dV) query rows without keys give P = 0
+    const int sbase = t0 + kb;      // first streamed row of the step
+    f32x4 pv[2], dsv[2];
+    if constexpr (!KEYS) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = sbase + 16 * kb2 + 4 * lg + i;
+          float pr = __builtin_amdgcn_exp2f(fmaf(xs[kb2][i], c2, -l2_row));
+          pr = key < Nkv ? pr : 0.f;
+          pv[kb2][i] = pr;
+          dsv[kb2][i] = pr * (ys[kb2][i] - d_row);
+        }
+    } else {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const int q0 = sbase + 16 * kb2 + 4 * lg;       // queries q0 .. q0 + 3
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int qq = q0 + i;
+          const int qc = qq < Nq ? qq : Nq - 1;
+          const float lse = LSE[qc];
+          const float l2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
+          float pr = __builtin_amdgcn_exp2f(fmaf(xs[kb2][i], c2, -l2));
+          pr = qq < Nq ? pr : 0.f;
+          pv[kb2][i] = pr;
+          dsv[kb2][i] = pr * (ys[kb2][i] - DEL[qc]);
+        }
+      }
+    }
+    // products over the 32 streamed rows: acc0 += T0^T (dS or P) ; acc1 ...
+    //  dQ kernel:    dQ^T += K^T dS^T        (T0 = K tile, transposed reads)
+    //  dK/dV kernel: dK^T += Q^T dS, dV^T += G^T P
+    if constexpr (BF16) {
+      bf16x8 dsf, pf;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dsf[i] = (__bf16)dsv[0][i];
+        dsf[4 + i] = (__bf16)dsv[1][i];
+        pf[i] = (__bf16)pv[0][i];
+        pf[4 + i] = (__bf16)pv[1][i];
+      }
+      constexpr int VO = G * TL + kb * RB;
+      constexpr int NR = KEYS ? 4 : 2;          // transposing reads per d block
+      auto issue = [&](auto e_, i16x4 (&r)[4]) __attribute__((always_inline)) {
+        constexpr int e = decltype(e_)::value;
+        r[0] = lds_read_tr<VO>(trl[e]);
+        r[1] = lds_read_tr<VO + 16 * RB>(trl[e]);
+        if constexpr (KEYS) {
+          r[2] = lds_read_tr<VO + 2 * TL>(trl[e]);
+          r[3] = lds_read_tr<VO + 2 * TL + 16 * RB>(trl[e]);
+        }
+      };
+      i16x4 buf[3][4];
+      issue(std::integral_constant<int, 0>{}, buf[0]);
+      if constexpr (ND > 1) issue(std::integral_constant<int, 1>{}, buf[1]);
+      static_for<0, ND>([&](auto e_) __attribute__((always_inline)) {
+        constexpr int e = decltype(e_)::value;
+        i16x4(&cur)[4] = buf[e % 3];
+        if constexpr (e + 2 < ND) {
+          issue(std::integral_constant<int, e + 2>{}, buf[(e + 2) % 3]);
+          lds_tr_wait<2 * NR>(cur[0], cur[1], cur[2], cur[3]);
+        } else if constexpr (e + 1 < ND) {
+          lds_tr_wait<NR>(cur[0], cur[1], cur[2], cur[3]);
+        } else {
+          lds_tr_wait<0>(cur[0], cur[1], cur[2], cur[3]);
+        }
+        const FragV t0f = __builtin_bit_cast(FragV, __builtin_shufflevector(cur[0], cur[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        acc0[e] = EV::mfma(t0f, dsf, acc0[e]);
+        if constexpr (KEYS) {
+          const FragV t1f = __builtin_bit_cast(FragV, __builtin_shufflevector(cur[2], cur[3], 0, 1, 2, 3, 4, 5, 6, 7));
+          acc1[e] = EV::mfma(t1f, pf, acc1[e]);
+        }
+      });
+    } else {
+      // float32: k-step (kb2, i) takes streamed row 16 kb2 + 4 lg + i
+      const char *Ts = smem + G * TL;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = kb + 16 * kb2 + 4 * lg + i;
+#pragma unroll
+          for (int e = 0; e < ND; ++e) {
+            const int o = lds_off<RB, true>(r, (16 * e + rl) * 4);
+            const FragV t0f = *(const FragV *)(Ts + o);
+            acc0[e] = EV::mfma(t0f, dsv[kb2][i], acc0[e]);
+            if constexpr (KEYS) {
+              const FragV t1f = *(const FragV *)(Ts + 2 * TL + o);
+              acc1[e] = EV::mfma(t1f, pv[kb2][i], acc1[e]);
+            }
+          }
+        }
+    }
+  };
+
+  auto tile = [&](auto G_, int it) __attribute__((always_inline)) {
+    wait_vmem();
+    __syncthreads();   // tile `it` landed; every wave is done with tile it-1
+    if (it + 1 < ntile) issue_tile(it + 1, 1 - decltype(G_)::value);
+    static_for<0, NSTEP>([&](auto kc) __attribute__((always_inline)) { step(G_, kc, it * BN); });
+  };
+
+  int it = 0;
+  for (; it + 1 < ntile; it += 2) {
+    tile(std::integral_constant<int, 0>{}, it);
+    tile(std::integral_constant<int, 1>{}, it + 1);
+  }
+  if (it < ntile) tile(std::integral_constant<int, 0>{}, it);
+
+  // epilogue: dQ = s dQ^T, dK = s dK^T, dV = dV^T
+  if (rvalid) {
+    typedef T T4 __attribute__((ext_vector_type(4)));
+    T *O0 = KEYS ? (T *)p.gk + b * p.sgk[0] + h * p.sgk[1] + (int64_t)row * p.sgk[2]
+                 : (T *)p.gq + b * p.sgq[0] + h * p.sgq[1] + (int64_t)row * p.sgq[2];
+#pragma unroll
+    for (int e = 0; e < ND; ++e) {
+      T4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = (T)(acc0[e][i] * p.scale);
+      *(T4 *)(O0 + 16 * e + 4 * lg) = o;
+    }
+    if constexpr (KEYS) {
+      T *O1 = (T *)p.gv + b * p.sgv[0] + h * p.sgv[1] + (int64_t)row * p.sgv[2];
+#pragma unroll
+      for (int e = 0; e < ND; ++e) {
+        T4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = (T)acc1[e][i];
+        *(T4 *)(O1 + 16 * e + 4 * lg) = o;
+      }
+    }
+  }
+}
+
+// dQ (and D) first, then dK and dV, on one stream.
+template <typename T, int D>
+hipError_t launch_bwd_instance(const BwdParams &p, hipStream_t s) {
+  using C = BwdCfg<T, D>;
+  hipLaunchKernelGGL((bwd_kernel<T, D, false>), dim3(p.B * p.H * p.nqb), dim3(64 * C::kWavesDq),
+                     0, s, p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((bwd_kernel<T, D, true>), dim3(p.B * p.H * p.nkb), dim3(64 * C::kWavesDkv),
+                     0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace attn_jvp

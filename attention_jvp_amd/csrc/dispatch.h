@@ -35,4 +35,11 @@ struct MergeParams {
 };
 hipError_t launch_merge(const MergeParams &m, bool bf16, hipStream_t s);
 
+// Primal backward (inst_bwd.hip, kernels in bwd.h): d_qk = d_v = d.
+struct BwdParams;
+hipError_t launch_bwd(const BwdParams &p, bool bf16, int d, hipStream_t s);
+// Query rows per dQ workgroup and key rows per dK/dV workgroup; false if
+// (dtype, d) is not built.
+bool bwd_shape_for(bool bf16, int d, int *block_q, int *block_k);
+
 }  // namespace attn_jvp

@@ -60,11 +60,12 @@ def visible_pairs(N, mask):
 
 
 def kernel_sha():
-    """sha256 over the sources of the attention kernel itself: the template
-    (kernel.h) and its instance units (inst.h, inst_*.hip), by name."""
+    """sha256 over the sources of the forward attention kernel itself: the
+    template (kernel.h) and its instance units (inst.h, inst_bf16_*.hip,
+    inst_fp32.hip), by name."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(KERNEL_SOURCES)):
-        if name == "kernel.h" or name.startswith("inst"):
+        if name in ("kernel.h", "inst.h", "inst_fp32.hip") or name.startswith("inst_bf16_"):
             h.update(name.encode())
             with open(os.path.join(KERNEL_SOURCES, name), "rb") as f:
                 h.update(f.read())

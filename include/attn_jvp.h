@@ -199,6 +199,41 @@ int attn_jvp_fwd_splitkv(const void *Q, const void *K, const void *V,
                          const attn_jvp_mask *mask, int num_splits,
                          void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---- Primal backward --------------------------------------------------
+ * Gradients of a loss L through O = softmax(s Q K^T) V, from the row
+ * log-sum-exp the forward stored (page "带分数正则的一致性蒸馏", section 注意力,
+ * subsection 反向): with gO = dL/dO,
+ *   P = exp(s Q K^T - LSE),   gV = P^T gO,   dP = gO V^T,
+ *   D = rowsum(gO (.) O),     dS = P (.) (dP - D),
+ *   gQ = s dS K,              gK = s dS^T Q.
+ * The tangents play no part (they are not trained).  As on the pages, the
+ * backward is built for d_qk == d_v only (otherwise ATTN_JVP_EUNSUPPORTED);
+ * Lq may differ from Lkv.  No mask. */
+
+/* Element strides (batch, head, row) of the backward's tensors. */
+typedef struct {
+  int64_t q[3], k[3], v[3], o[3], go[3];   /* inputs */
+  int64_t gq[3], gk[3], gv[3];             /* outputs */
+} attn_jvp_bwd_layout;
+
+/* gQ [B,H,Lq,d], gK, gV [B,H,Lkv,d] (the dtype) from Q, K, V, O, gO (the
+ * dtype) and LSE (float32 [B,H,Lq], as the forward wrote it).  delta is a
+ * caller-owned float32 [B,H,Lq] buffer that receives D = rowsum(gO (.) O).
+ * `layout` NULL means every tensor contiguous in its shape.  scale <= 0
+ * selects 1/sqrt(d).  Two launches on `stream` (dQ and D, then dK and dV);
+ * deterministic (no atomics).  Outputs must not overlap inputs or each
+ * other.  Returns a status; nothing is launched unless it is ATTN_JVP_OK. */
+int attn_jvp_bwd(const void *Q, const void *K, const void *V, const void *O,
+                 const void *gO, const float *LSE, void *gQ, void *gK, void *gV,
+                 float *delta, const attn_jvp_shape *shape, float scale, int dtype,
+                 const attn_jvp_bwd_layout *layout, void *stream);
+
+/* Host-only argument check of attn_jvp_bwd (never touches the GPU). */
+int attn_jvp_bwd_check(const void *Q, const void *K, const void *V, const void *O,
+                       const void *gO, const float *LSE, void *gQ, void *gK,
+                       void *gV, float *delta, const attn_jvp_shape *shape,
+                       int dtype, const attn_jvp_bwd_layout *layout);
+
 /* Contiguous [B, H, N, d] tensors.  scale <= 0 selects 1/sqrt(d).
  * Returns an attn_jvp_status. */
 int attn_jvp_fwd(const void *Q, const void *K, const void *V,

@@ -231,3 +231,36 @@ def test_long_video_visited_fraction():
     got = aj.attn_jvp_visible_tiles(65520, 0, 128, mask)
     total = len(got) * ((65520 + 63) // 64)
     assert 0.36 < sum(got) / total < 0.38
+
+
+def _bwd_ptrs(B, H, Nq, Nkv, d, esize):
+    sizes = [B * H * n * d * esize for n in (Nq, Nkv, Nkv, Nq, Nq)] + [B * H * Nq * 4] + \
+        [B * H * n * d * esize for n in (Nq, Nkv, Nkv)] + [B * H * Nq * 4]
+    base, p = 1 << 40, []
+    for sz in sizes:
+        p.append(base)
+        base += (sz + 255) // 256 * 256
+    return p
+
+
+def test_bwd_check():
+    shape = aj.Shape(2, 3, 100, 260, 128, 128)
+    p = _bwd_ptrs(2, 3, 100, 260, 128, 2)
+    assert aj.attn_jvp_bwd_check(*p, shape, 0) == 0
+    for d in (16, 32, 64, 256):
+        sh = aj.Shape(1, 2, 50, 70, d, d)
+        assert aj.attn_jvp_bwd_check(*_bwd_ptrs(1, 2, 50, 70, d, 2), sh, 0) == 0, d
+    assert aj.attn_jvp_bwd_check(*_bwd_ptrs(1, 2, 50, 70, 64, 4), aj.Shape(1, 2, 50, 70, 64, 64), 1) == 0
+    assert aj.attn_jvp_bwd_check(*p, aj.Shape(2, 3, 100, 260, 128, 64), 0) == -2   # d_qk != d_v
+    assert aj.attn_jvp_bwd_check(*p, aj.Shape(2, 3, 100, 260, 96, 96), 0) == -2
+    assert aj.attn_jvp_bwd_check(*_bwd_ptrs(1, 2, 50, 70, 128, 4), aj.Shape(1, 2, 50, 70, 128, 128), 1) == -2
+    assert aj.attn_jvp_bwd_check(*p, aj.Shape(2, 3, 0, 260, 128, 128), 0) == -1
+    q = list(p)
+    q[5] = None                                     # LSE
+    assert aj.attn_jvp_bwd_check(*q, shape, 0) == -1
+    q = list(p)
+    q[6] = p[0] + 512                               # dQ overlaps Q
+    assert aj.attn_jvp_bwd_check(*q, shape, 0) == -3
+    q = list(p)
+    q[9] = p[5]                                     # delta overlaps LSE
+    assert aj.attn_jvp_bwd_check(*q, shape, 0) == -3
