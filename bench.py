@@ -11,7 +11,11 @@ Q dK^T over d_qk; P V, P dV, (P . dS) V over d_v), 12 N^2 d when square.
 ``--shape B,H,Lq,Lkv,d_qk,d_v`` times a synthetic shape instead of a named
 workload (Gaussian inputs, tangents x 0.1); ``--splitkv S`` times the
 split-KV path (attn_jvp_fwd_splitkv with S splits, 0 = the library's
-choice; the workspace is allocated once, outside the timed region).
+choice; the workspace is allocated once, outside the timed region);
+``--backward`` times the primal backward (attn_jvp_bwd) instead, on O and
+LSE from one forward call and a Gaussian dL/dO, counting the algorithmic
+10 * Lq * Lkv * d FLOPs per (batch, head) (S, dP, dV, dK, dQ; the
+recomputation of S and dP in the second launch is not counted).
 
 Prints one JSON line.  ``--gpus`` above 1 is refused: this path runs on one
 GPU.
@@ -148,6 +152,8 @@ def main():
                     help="time this synthetic shape instead of a named workload")
     ap.add_argument("--splitkv", type=int, default=-1, metavar="S",
                     help="time attn_jvp_fwd_splitkv with S key splits (0 = library choice)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the primal backward (attn_jvp_bwd) instead of the JVP")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target length of the timed oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -200,8 +206,19 @@ def main():
         ws = torch.empty(max(need, 256), device="cuda", dtype=torch.uint8)
         log(f"split-KV: {splits} splits, workspace {need} bytes")
 
+    if args.backward:
+        if mask is not None or splits is not None or w.dv != w.d:
+            print("--backward: dense, one head dim, no split-KV", file=sys.stderr)
+            sys.exit(2)
+        aj.fwd(*g, out=outs)
+        go = torch.randn(o.shape, generator=torch.Generator().manual_seed(7)).to(o.dtype).cuda()
+        grads = (torch.empty_like(g[0]), torch.empty_like(g[1]), torch.empty_like(g[2]),
+                 torch.empty_like(lse))
+
     def step():
-        if splits is None:
+        if args.backward:
+            aj.bwd(g[0], g[1], g[2], o, go, lse, out=grads)
+        elif splits is None:
             aj.fwd(*g, mask=mask, out=outs)
         else:
             aj.fwd_splitkv(*g, mask=mask, num_splits=splits, workspace=ws, out=outs)
@@ -220,18 +237,21 @@ def main():
     ms = start.elapsed_time(end) / args.steps
     pairs = visible_pairs(w.N, mask) if mask is not None else w.N * w.Nkv
     flops = 6.0 * w.B * w.H * pairs * (w.d + w.dv)
+    if args.backward:
+        flops = 10.0 * w.B * w.H * pairs * w.d
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     log(f"{ms:.4f} ms/step, {tflops:.1f} TFLOP/s ({100 * tflops / peak:.1f}% of {peak} peak)")
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.backward:
         log("timing the float64 oracle on a row sample")
         cpu = cpu_baseline(w, x, args.cpu_seconds)
         log(f"oracle: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads")
 
     line = {
-        "metric": METRIC,
+        "metric": METRIC if not args.backward else
+        "attention primal backward TFLOP/s (dQ, dK, dV) and % of bf16 MFMA peak, 1 GPU",
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -248,6 +268,7 @@ def main():
             "workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
             **({"Lkv": w.Nkv, "d_v": w.dv} if (w.Nkv != w.N or w.dv != w.d) else {}),
             **({"splitkv": splits} if splits is not None else {}),
+            **({"pass": "backward"} if args.backward else {}),
             "mask": mask, "visible_pairs_per_head": pairs,
             "counted_flops": flops,
         },
@@ -257,7 +278,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(tflops / peak, 4),
-            "traffic": traffic_record(w.name) if splits is None else None,
+            "traffic": traffic_record(w.name) if splits is None and not args.backward else None,
         },
         "cpu_baseline": cpu,
     }
