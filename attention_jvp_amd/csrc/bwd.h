@@ -96,7 +96,7 @@ struct BwdCfg {
   static constexpr int kResDq = (ES == 2 ? D / 4 : D / 2) + D / 4;
   static constexpr int kResDkv = (ES == 2 ? D / 4 : D / 2) + D / 2;
   static constexpr int kWavesDq = kResDq <= 96 ? 8 : 4;
-  static constexpr int kWavesDkv = kResDkv <= 96 ? 8 : 4;
+  static constexpr int kWavesDkv = kResDkv <= (ES == 2 ? 96 : 48) ? 8 : 4;
   // 64-row tiles while two stages of both tensors fit in 128 KiB and the
   // transposing reads' largest constant offset (stage, second tensor, row
   // 48 of the tile) fits the 16-bit DS offset field; else 32
@@ -124,7 +124,8 @@ void bwd_kernel(BwdParams p) {
   constexpr int ND = D / 16;
   constexpr float kLog2e = 1.4426950408889634f;
 
-  __shared__ __attribute__((aligned(1024))) char smem[C::kLds];
+  // tiles, then (dK/dV kernel) two stages x 3 rows of 64 floats of query terms
+  __shared__ __attribute__((aligned(1024))) char smem[C::kLds + (KEYS ? 2 * 3 * 256 : 0)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -169,8 +170,23 @@ void bwd_kernel(BwdParams p) {
   // one swizzle (the operand-row rule) serves both
   PairCopier<T, RB, BN, W> copier;
   copier.init(S0, S1, ss0, ss1, wave, lane);
+  // dK/dV kernel: the streamed query rows' LSE and D come with the tile, as
+  // 4-byte global->LDS copies (64 rows per wave instruction): wave 0 copies
+  // LSE, wave 1 D, the other waves a dummy row (no branch around the copies,
+  // which keeps the compiler from waiting for them before every LDS read).
+  // Rows are clamped to Nq - 1 (their P is masked to 0).
+  // (row `which` of stage g at smem + kLds + (3 g + which) 256)
   auto issue_tile = [&](int it, int g) __attribute__((always_inline)) {
     copier.issue(it * BN, Nstr, smem + g * TL, 2 * TL);
+    if constexpr (KEYS) {
+      int qr = it * BN + lane;
+      qr = qr < Nq ? qr : Nq - 1;
+      const int which = wave < 2 ? wave : 2;
+      const float *src = (which == 1 ? DEL : LSE) + qr;
+      __builtin_amdgcn_global_load_lds((const void *)src,
+                                       (lds_void *)(smem + C::kLds + (3 * g + which) * 256), 4,
+                                       0, 0);
+    }
   };
   issue_tile(0, 0);
 
@@ -278,16 +294,17 @@ void bwd_kernel(BwdParams p) {
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         const int q0 = sbase + 16 * kb2 + 4 * lg;       // queries q0 .. q0 + 3
+        const float *qt = (const float *)(smem + C::kLds + 3 * G * 256) + kb + 16 * kb2 + 4 * lg;
+        const f32x4 lse4 = *(const f32x4 *)qt;
+        const f32x4 del4 = *(const f32x4 *)(qt + 64);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int qq = q0 + i;
-          const int qc = qq < Nq ? qq : Nq - 1;
-          const float lse = LSE[qc];
-          const float l2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
+          const float l2 = lse4[i] == -INFINITY ? INFINITY : lse4[i] * kLog2e;
           float pr = __builtin_amdgcn_exp2f(fmaf(xs[kb2][i], c2, -l2));
           pr = qq < Nq ? pr : 0.f;
           pv[kb2][i] = pr;
-          dsv[kb2][i] = pr * (ys[kb2][i] - DEL[qc]);
+          dsv[kb2][i] = pr * (ys[kb2][i] - del4[i]);
         }
       }
     }
