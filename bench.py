@@ -152,6 +152,8 @@ def main():
                     help="time this synthetic shape instead of a named workload")
     ap.add_argument("--splitkv", type=int, default=-1, metavar="S",
                     help="time attn_jvp_fwd_splitkv with S key splits (0 = library choice)")
+    ap.add_argument("--flush", action="store_true",
+                    help="also time launches after writing 512 MiB (evicts L2 and MALL)")
     ap.add_argument("--backward", action="store_true",
                     help="time the primal backward (attn_jvp_bwd) instead of the JVP")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -235,6 +237,29 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
+
+    # per-launch times over a second run of the same number of steps (median,
+    # minimum), and optionally with L2/MALL evicted before each launch
+    def per_launch(before=None):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a, b in evs:
+            if before is not None:
+                before()
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in evs)
+
+    per = per_launch()
+    timing = {"ms_mean": round(ms, 5), "ms_median": round(per[len(per) // 2], 5),
+              "ms_min": round(per[0], 5)}
+    if args.flush:
+        junk = torch.empty(512 << 20, device="cuda", dtype=torch.uint8)
+        cold = per_launch(lambda: junk.zero_())
+        timing["ms_median_cold_l2_mall"] = round(cold[len(cold) // 2], 5)
+        del junk
     pairs = visible_pairs(w.N, mask) if mask is not None else w.N * w.Nkv
     flops = 6.0 * w.B * w.H * pairs * (w.d + w.dv)
     if args.backward:
@@ -281,6 +306,7 @@ def main():
             "traffic": traffic_record(w.name) if splits is None and not args.backward else None,
         },
         "cpu_baseline": cpu,
+        "timing": timing,
     }
     print(json.dumps(line), flush=True)
 
