@@ -23,6 +23,8 @@
 //     streams in while the current one is consumed; no register staging),
 //     row-major with an XOR swizzle of the 16-byte chunks (one rule for the
 //     operand-row reads of K and dK, one for the transposing reads of V, dV);
+//   * the score products read their K and dK slices two or three slices
+//     ahead of the MFMAs that use them, with explicit LDS waits;
 //   * the value products need V and dV transposed (keys along the MFMA k
 //     dimension): ds_read_b64_tr_b16 transposes on the way out of LDS;
 //   * O^T, A^T, B^T accumulate in 16x16 fp32 fragments that belong to the
@@ -302,6 +304,26 @@ __device__ inline void lds_tr_wait(i16x4 &a, i16x4 &b, i16x4 &c, i16x4 &d) {
   asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "n"(N));
 }
 
+// K-side operand read (one 16-byte row slice of K or dK), issued through
+// inline asm for the reason given at lds_read_tr; lds_pair_wait<N> waits
+// until at most N LDS operations are outstanding and passes the two values
+// through the asm, so that no MFMA reading them is scheduled before it.
+// Holding the reads in flight this way lets the score MFMAs of one slice
+// run while the next slices are still on their way from LDS.
+template <int OFF>
+__device__ inline bf16x8 lds_read_k(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "DS offset field");
+  bf16x8 v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
+  return v;
+}
+
+template <int N>
+__device__ inline void lds_pair_wait(bf16x8 &a, bf16x8 &b) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt field");
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
+}
+
 // Sum and maximum over the four lanes l, l^16, l^32, l^48 that hold one
 // query row.  v_permlane16_swap(x, x) returns rows (x0, x0, x2, x2) and
 // (x1, x1, x3, x3) of x's four 16-lane rows, and v_permlane32_swap(x, x)
@@ -571,20 +593,52 @@ __global__ __launch_bounds__((Cfg<T, DQK, DV>::kThreads), 1) void attn_jvp_kerne
                     __attribute__((always_inline)) {
     constexpr int G = decltype(G_)::value;
     constexpr int kb = decltype(KC_)::value * CK;
+    if constexpr (BF16 && DQK >= 32) {
+      // slices j = (kb2, s), kb2-major, each a K and a dK read; PD slices in
+      // flight (the wait before slice j leaves the later ones outstanding)
+      constexpr int NP = 2 * DS;
+      constexpr int PD0 = DQK >= 128 ? 3 : 2;
+      constexpr int PD = PD0 < NP ? PD0 : NP;
+      bf16x8 kf[NP], dkf[NP];
+      auto issue = [&](auto j_) __attribute__((always_inline)) {
+        constexpr int j = decltype(j_)::value;
+        constexpr int kb2 = j / DS, s = j % DS;
+        constexpr int OFF = G * TK + (kb + 16 * kb2) * RBK;
+        kf[j] = lds_read_k<OFF>(kl[s]);
+        dkf[j] = lds_read_k<OFF + 2 * TK>(kl[s]);
+      };
+      static_for<0, PD - 1>([&](auto j_) __attribute__((always_inline)) { issue(j_); });
+      f32x4 s_[2] = {f32x4{}, f32x4{}}, ds_[2] = {f32x4{}, f32x4{}};
+      static_for<0, NP>([&](auto j_) __attribute__((always_inline)) {
+        constexpr int j = decltype(j_)::value;
+        constexpr int kb2 = j / DS, s = j % DS;
+        if constexpr (j + PD - 1 < NP) issue(std::integral_constant<int, j + PD - 1>{});
+        constexpr int newer = (NP - 1 - j) < (PD - 1) ? (NP - 1 - j) : (PD - 1);
+        lds_pair_wait<2 * newer>(kf[j], dkf[j]);
+        s_[kb2] = EK::mfma(kf[j], qf[s], s_[kb2]);
+        ds_[kb2] = EK::mfma(kf[j], dqf[s], ds_[kb2]);
+        ds_[kb2] = EK::mfma(dkf[j], qf[s], ds_[kb2]);
+      });
+      sacc[0] = s_[0];
+      sacc[1] = s_[1];
+      dsacc[0] = ds_[0];
+      dsacc[1] = ds_[1];
+    } else {
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      f32x4 s_ = f32x4{}, ds_ = f32x4{};
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        f32x4 s_ = f32x4{}, ds_ = f32x4{};
 #pragma unroll
-      for (int s = 0; s < DS; ++s) {
-        const char *kp = smem + (kl[s] - smem_a) + G * TK + (kb + 16 * kb2) * RBK;
-        const FragK kf = *(const FragK *)kp;
-        const FragK dkf = *(const FragK *)(kp + 2 * TK);
-        s_ = EK::mfma(kf, qf[s], s_);
-        ds_ = EK::mfma(kf, dqf[s], ds_);
-        ds_ = EK::mfma(dkf, qf[s], ds_);
+        for (int s = 0; s < DS; ++s) {
+          const char *kp = smem + (kl[s] - smem_a) + G * TK + (kb + 16 * kb2) * RBK;
+          const FragK kf = *(const FragK *)kp;
+          const FragK dkf = *(const FragK *)(kp + 2 * TK);
+          s_ = EK::mfma(kf, qf[s], s_);
+          ds_ = EK::mfma(kf, dqf[s], ds_);
+          ds_ = EK::mfma(dkf, qf[s], ds_);
+        }
+        sacc[kb2] = s_;
+        dsacc[kb2] = ds_;
       }
-      sacc[kb2] = s_;
-      dsacc[kb2] = ds_;
     }
   };
 
