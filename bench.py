@@ -17,6 +17,10 @@ LSE from one forward call and a Gaussian dL/dO, counting the algorithmic
 10 * Lq * Lkv * d FLOPs per (batch, head) (S, dP, dV, dK, dQ; the
 recomputation of S and dP in the second launch is not counted).
 
+The warm-up runs at least ``--warmup`` steps and at least 0.3 s of work, so
+the timed steps run at the sustained engine clock (``warmup_run`` in the
+JSON line is the number of warm-up steps actually run).
+
 Prints one JSON line.  ``--gpus`` above 1 is refused: this path runs on one
 GPU.
 """
@@ -34,6 +38,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention-JVP TFLOP/s (fwd+tangent) and % of bf16 MFMA peak, 1 GPU"
 # MI355X dense MFMA peaks, TFLOP/s
 PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}
+WARM_SECONDS = 0.3   # minimum warm-up before the timed steps
 NAMES = ("q", "k", "v", "dq", "dk", "dv")
 KERNEL_SOURCES = os.path.join(ROOT, "attention_jvp_amd", "csrc")
 
@@ -225,8 +230,16 @@ def main():
         else:
             aj.fwd_splitkv(*g, mask=mask, num_splits=splits, workspace=ws, out=outs)
 
-    for _ in range(args.warmup):
+    # warm-up: W steps, continued until WARM_SECONDS of work have run, so
+    # the timed steps see the sustained engine clock (a GPU coming out of idle
+    # ramps its clock over the first tens of milliseconds of work)
+    t_warm = time.perf_counter()
+    n_warm = 0
+    while n_warm < args.warmup or time.perf_counter() - t_warm < WARM_SECONDS:
         step()
+        n_warm += 1
+        if n_warm % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     start = torch.cuda.Event(enable_timing=True)
@@ -282,6 +295,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_run": n_warm,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
