@@ -16,6 +16,13 @@
 // global->LDS copies, two stages, swizzled rows) and transposing reads are
 // those of the forward kernel (kernel.h).  d_qk = d_v = D, as the pages
 // require for the backward.
+//
+// The VALU work per score is kept to the exponential, one FMA, one multiply
+// and the bf16 packs: the dP accumulators start at -D, so the MFMAs yield
+// dP - D; the dK/dV kernel reads each streamed query's -LSE log2 e (-inf for
+// rows past the end and for rows with no visible key, which makes P = 0) and
+// -D from LDS rows that two waves transform once per tile, a tile ahead of
+// use; the dQ kernel masks keys past the end only in the last tile.
 
 #pragma once
 
@@ -87,6 +94,20 @@ struct PairCopier {
   }
 };
 
+// 16-byte LDS read through inline asm (see lds_read_tr) and a wait for four
+// such values (at most N LDS operations left outstanding).
+__device__ inline f32x4 lds_read_f4(uint32_t addr) {
+  f32x4 v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
+}
+
+template <int N>
+__device__ inline void lds_quad_wait(f32x4 &a, f32x4 &b, f32x4 &c, f32x4 &d) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt field");
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "n"(N));
+}
+
 template <typename T, int D>
 struct BwdCfg {
   static constexpr int ES = (int)sizeof(T);
@@ -123,9 +144,12 @@ void bwd_kernel(BwdParams p) {
   constexpr int DS = D / KI;
   constexpr int ND = D / 16;
   constexpr float kLog2e = 1.4426950408889634f;
+  constexpr int kRowSlot = 3 * 256;    // bytes of one slot of query-term rows
 
-  // tiles, then (dK/dV kernel) two stages x 3 rows of 64 floats of query terms
-  __shared__ __attribute__((aligned(1024))) char smem[C::kLds + (KEYS ? 2 * 3 * 256 : 0)];
+  // tiles, then (dK/dV kernel) three slots x 3 rows of 64 floats of query
+  // terms: row 0 -LSE log2 e, row 1 -D, row 2 a landing row for the waves
+  // that copy neither
+  __shared__ __attribute__((aligned(1024))) char smem[C::kLds + (KEYS ? 3 * kRowSlot : 0)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -170,25 +194,48 @@ void bwd_kernel(BwdParams p) {
   // one swizzle (the operand-row rule) serves both
   PairCopier<T, RB, BN, W> copier;
   copier.init(S0, S1, ss0, ss1, wave, lane);
-  // dK/dV kernel: the streamed query rows' LSE and D come with the tile, as
-  // 4-byte global->LDS copies (64 rows per wave instruction): wave 0 copies
-  // LSE, wave 1 D, the other waves a dummy row (no branch around the copies,
-  // which keeps the compiler from waiting for them before every LDS read).
-  // Rows are clamped to Nq - 1 (their P is masked to 0).
-  // (row `which` of stage g at smem + kLds + (3 g + which) 256)
-  auto issue_tile = [&](int it, int g) __attribute__((always_inline)) {
-    copier.issue(it * BN, Nstr, smem + g * TL, 2 * TL);
+  // dK/dV kernel: the streamed query rows' LSE and D come as 4-byte
+  // global->LDS copies (64 rows per wave instruction) into slot it % 3, two
+  // tiles ahead of use: wave 0 copies LSE, wave 1 D, the other waves the
+  // landing row (no branch around the copies).  During tile it - 1, waves 0
+  // and 1 turn their row of tile it into -LSE log2 e and -D in place.  Rows
+  // are clamped to Nq - 1 for the copy; the transform gives them -inf.
+  const uint32_t rows_a = lds_addr(smem) + C::kLds;
+  auto issue_rows = [&](int it) __attribute__((always_inline)) {
     if constexpr (KEYS) {
       int qr = it * BN + lane;
       qr = qr < Nq ? qr : Nq - 1;
       const int which = wave < 2 ? wave : 2;
       const float *src = (which == 1 ? DEL : LSE) + qr;
-      __builtin_amdgcn_global_load_lds((const void *)src,
-                                       (lds_void *)(smem + C::kLds + (3 * g + which) * 256), 4,
-                                       0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const void *)src, (lds_void *)(smem + C::kLds + (it % 3) * kRowSlot + which * 256), 4,
+          0, 0);
     }
   };
+  auto transform_rows = [&](int it) __attribute__((always_inline)) {
+    if constexpr (KEYS) {
+      if (wave < 2) {
+        const uint32_t a = rows_a + (it % 3) * kRowSlot + wave * 256 + lane * 4;
+        float v;
+        asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a));
+        const int qr = it * BN + lane;
+        float t;
+        if (wave == 0) t = (qr < Nq && v != -INFINITY) ? -v * kLog2e : -INFINITY;
+        else t = -v;
+        asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(a), "v"(t) : "memory");
+      }
+    }
+  };
+  auto issue_tile = [&](int it, int g) __attribute__((always_inline)) {
+    copier.issue(it * BN, Nstr, smem + g * TL, 2 * TL);
+  };
   issue_tile(0, 0);
+  issue_rows(0);
+  if (ntile > 1) issue_rows(1);
+  if constexpr (KEYS) {
+    wait_vmem();
+    transform_rows(0);   // visible to all waves after the first tile's barrier
+  }
 
   // owned fragments (B operands): lane holds row rl, d-slice s KI + lg KL
   FragK af[DS], bf[DS];
@@ -252,62 +299,103 @@ void bwd_kernel(BwdParams p) {
       trl[e] = smem_a + lds_off<RB, true>(4 * lg + (rl >> 2), (16 * e + 4 * (rl & 3)) * 2);
   }
 
+  // dQ kernel: -LSE log2 e of the lane's query (-inf for a row with no
+  // visible key, so that P = 0 there) and the start value of its dP sums
+  const float nl2_row = KEYS ? 0.f : -l2_row;
+  const f32x4 nd_row = f32x4{-d_row, -d_row, -d_row, -d_row};
+
   // One 32-row step kc of the streamed tile in stage G.
-  //  dQ kernel:   X^T = K Q^T (keys x queries), Y^T = V G^T; lane: query rl,
-  //               keys 4 lg + i (+16 for the second half)
-  //  dK/dV kernel: X = Q K^T (queries x keys), Y = G V^T; lane: key rl,
+  //  dQ kernel:   X^T = K Q^T (keys x queries), Y^T = V G^T - D; lane: query
+  //               rl, keys 4 lg + i (+16 for the second half)
+  //  dK/dV kernel: X = Q K^T (queries x keys), Y = G V^T - D; lane: key rl,
   //               queries 4 lg + i (+16)
-  auto step = [&](auto G_, auto KC_, int t0) __attribute__((always_inline)) {
+  // rows: LDS address of the tile's query-term slot (dK/dV kernel); tail:
+  // the tile holds streamed rows past the end (dQ kernel masks those keys)
+  auto step = [&](auto G_, auto KC_, int t0, uint32_t rows, bool tail)
+                  __attribute__((always_inline)) {
     constexpr int G = decltype(G_)::value;
     constexpr int kb = decltype(KC_)::value * CK;
-    f32x4 xs[2], ys[2];
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      f32x4 x_ = f32x4{}, y_ = f32x4{};
-#pragma unroll
-      for (int s = 0; s < DS; ++s) {
-        const char *rp = smem + (rdl[s] - smem_a) + G * TL + (kb + 16 * kb2) * RB;
-        const FragK r0f = *(const FragK *)rp;
-        const FragK r1f = *(const FragK *)(rp + 2 * TL);
-        x_ = EK::mfma(r0f, af[s], x_);
-        y_ = EK::mfma(r1f, bf[s], y_);
-      }
-      xs[kb2] = x_;
-      ys[kb2] = y_;
-    }
-    // P and dS = P (.) (dP - D), unscaled; streamed rows past the end and
-    // (dK/dV) query rows without keys give P = 0
-    const int sbase = t0 + kb;      // first streamed row of the step
-    f32x4 pv[2], dsv[2];
-    if constexpr (!KEYS) {
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = sbase + 16 * kb2 + 4 * lg + i;
-          float pr = __builtin_amdgcn_exp2f(fmaf(xs[kb2][i], c2, -l2_row));
-          pr = key < Nkv ? pr : 0.f;
-          pv[kb2][i] = pr;
-          dsv[kb2][i] = pr * (ys[kb2][i] - d_row);
-        }
-    } else {
+    f32x4 nl2[2], y0[2];
+    if constexpr (KEYS) {
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
-        const int q0 = sbase + 16 * kb2 + 4 * lg;       // queries q0 .. q0 + 3
-        const float *qt = (const float *)(smem + C::kLds + 3 * G * 256) + kb + 16 * kb2 + 4 * lg;
-        const f32x4 lse4 = *(const f32x4 *)qt;
-        const f32x4 del4 = *(const f32x4 *)(qt + 64);
+        const uint32_t a = rows + (kb + 16 * kb2 + 4 * lg) * 4;
+        nl2[kb2] = lds_read_f4(a);
+        y0[kb2] = lds_read_f4(a + 256);
+      }
+    } else {
+      y0[0] = nd_row;
+      y0[1] = nd_row;
+    }
+    f32x4 xs[2], ys[2];
+    if constexpr (BF16 && D >= 32) {
+      // slices j = (kb2, s), kb2-major, each a tensor-0 and a tensor-1 read;
+      // PD slices in flight
+      constexpr int NP = 2 * DS;
+      constexpr int PD0 = D >= 128 ? 3 : 2;
+      constexpr int PD = PD0 < NP ? PD0 : NP;
+      bf16x8 r0f[NP], r1f[NP];
+      auto issue = [&](auto j_) __attribute__((always_inline)) {
+        constexpr int j = decltype(j_)::value;
+        constexpr int kb2 = j / DS, s = j % DS;
+        constexpr int OFF = G * TL + (kb + 16 * kb2) * RB;
+        r0f[j] = lds_read_k<OFF>(rdl[s]);
+        r1f[j] = lds_read_k<OFF + 2 * TL>(rdl[s]);
+      };
+      static_for<0, PD - 1>([&](auto j_) __attribute__((always_inline)) { issue(j_); });
+      if constexpr (KEYS) lds_quad_wait<2 * (PD - 1)>(nl2[0], nl2[1], y0[0], y0[1]);
+      f32x4 x_[2] = {f32x4{}, f32x4{}}, y_[2] = {y0[0], y0[1]};
+      static_for<0, NP>([&](auto j_) __attribute__((always_inline)) {
+        constexpr int j = decltype(j_)::value;
+        constexpr int kb2 = j / DS, s = j % DS;
+        if constexpr (j + PD - 1 < NP) issue(std::integral_constant<int, j + PD - 1>{});
+        constexpr int newer = (NP - 1 - j) < (PD - 1) ? (NP - 1 - j) : (PD - 1);
+        lds_pair_wait<2 * newer>(r0f[j], r1f[j]);
+        x_[kb2] = EK::mfma(r0f[j], af[s], x_[kb2]);
+        y_[kb2] = EK::mfma(r1f[j], bf[s], y_[kb2]);
+      });
+      xs[0] = x_[0];
+      xs[1] = x_[1];
+      ys[0] = y_[0];
+      ys[1] = y_[1];
+    } else {
+      if constexpr (KEYS) lds_quad_wait<0>(nl2[0], nl2[1], y0[0], y0[1]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int qq = q0 + i;
-          const float l2 = lse4[i] == -INFINITY ? INFINITY : lse4[i] * kLog2e;
-          float pr = __builtin_amdgcn_exp2f(fmaf(xs[kb2][i], c2, -l2));
-          pr = qq < Nq ? pr : 0.f;
-          pv[kb2][i] = pr;
-          dsv[kb2][i] = pr * (ys[kb2][i] - del4[i]);
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        f32x4 x_ = f32x4{}, y_ = y0[kb2];
+#pragma unroll
+        for (int s = 0; s < DS; ++s) {
+          const char *rp = smem + (rdl[s] - smem_a) + G * TL + (kb + 16 * kb2) * RB;
+          const FragK r0f = *(const FragK *)rp;
+          const FragK r1f = *(const FragK *)(rp + 2 * TL);
+          x_ = EK::mfma(r0f, af[s], x_);
+          y_ = EK::mfma(r1f, bf[s], y_);
         }
+        xs[kb2] = x_;
+        ys[kb2] = y_;
       }
     }
+    // P and dS = P (.) (dP - D), unscaled
+    f32x4 pv[2], dsv[2];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        pv[kb2][i] = __builtin_amdgcn_exp2f(fmaf(xs[kb2][i], c2, KEYS ? nl2[kb2][i] : nl2_row));
+    if constexpr (!KEYS) {
+      if (tail) {
+        const int sbase = t0 + kb;   // first key of the step
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            pv[kb2][i] = sbase + 16 * kb2 + 4 * lg + i < Nkv ? pv[kb2][i] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dsv[kb2][i] = pv[kb2][i] * ys[kb2][i];
     // products over the 32 streamed rows: acc0 += T0^T (dS or P) ; acc1 ...
     //  dQ kernel:    dQ^T += K^T dS^T        (T0 = K tile, transposed reads)
     //  dK/dV kernel: dK^T += Q^T dS, dV^T += G^T P
@@ -378,7 +466,15 @@ void bwd_kernel(BwdParams p) {
     wait_vmem();
     __syncthreads();   // tile `it` landed; every wave is done with tile it-1
     if (it + 1 < ntile) issue_tile(it + 1, 1 - decltype(G_)::value);
-    static_for<0, NSTEP>([&](auto kc) __attribute__((always_inline)) { step(G_, kc, it * BN); });
+    if constexpr (KEYS) {
+      if (it + 2 < ntile) issue_rows(it + 2);
+      if (it + 1 < ntile) transform_rows(it + 1);
+    }
+    const uint32_t rows = rows_a + (it % 3) * kRowSlot;
+    const bool tail = (it + 1) * BN > Nstr;
+    static_for<0, NSTEP>([&](auto kc) __attribute__((always_inline)) {
+      step(G_, kc, it * BN, rows, tail);
+    });
   };
 
   int it = 0;

@@ -84,6 +84,36 @@ def test_backward_image_dit_shape_sampled():
     _check(w, what="bwd 1x2x4096x128")
 
 
+@pytest.mark.parametrize("dtype,d,Nq,Nkv", [("bf16", 128, 150, 333), ("bf16", 64, 97, 70),
+                                           ("fp32", 32, 130, 40)])
+def test_backward_rows_without_keys(dtype, d, Nq, Nkv):
+    # a forward whose rows 0, 5, 6 and the last see no key stores LSE = -inf
+    # and O = 0 there; the backward must give those rows P = 0 (dQ row 0, no
+    # contribution to dK, dV) and the other rows their unmasked gradients
+    w = Workload("bwdz", 1, 2, Nq, d, dtype, 9600 + d + Nq, tangent_scale=0.1, n_kv=Nkv)
+    x = make_inputs(w)
+    empty = np.array([0, 5, 6, Nq - 1])
+    vis = lambda qi, ki: ~np.isin(qi, empty)[:, None] & np.ones((1, len(ki)), dtype=bool)
+    o64, _, lse64, _ = attention_jvp(*(to_float64(x[n]) for n in NAMES), visible=vis)
+    assert np.isneginf(lse64[:, :, empty]).all() and np.isfinite(lse64[:, :, 1]).all()
+    q, k, v = (x[n].cuda() for n in ("q", "k", "v"))
+    o = torch.from_numpy(o64).to(q.dtype).cuda()
+    lse = torch.from_numpy(lse64).float().cuda()
+    g_cpu = _grad_input(w, w.seed + 1)
+    gq, gk, gv, delta = aj.bwd(q, k, v, o, g_cpu.cuda(), lse)
+    torch.cuda.synchronize()
+    ref = attention_backward(to_float64(x["q"]), to_float64(x["k"]), to_float64(x["v"]),
+                             to_float64(g_cpu), visible=vis)
+    errs = {}
+    for n, a, r in zip(("dQ", "dK", "dV"), (gq, gk, gv), ref):
+        a64 = to_float64(a)
+        assert np.isfinite(a64).all(), f"{n} not finite"
+        errs[n] = _err(a64, r)
+        assert errs[n] <= TOL[dtype], f"{n} normwise error {errs[n]:.3e}"
+    assert np.all(to_float64(gq)[:, :, empty] == 0.0)
+    _say(f"bwd rows without keys {dtype} d{d}", " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+
+
 def test_backward_deterministic():
     w = Workload("bwdd", 1, 2, 500, 128, "bf16", 9400, tangent_scale=0.1, n_kv=700)
     x = make_inputs(w)
