@@ -301,6 +301,7 @@ __device__ __attribute__((always_inline)) inline void static_for(F &&f) {
 // through the asm so that nothing reading them can be scheduled before it.
 template <int N>
 __device__ inline void lds_tr_wait(i16x4 &a, i16x4 &b, i16x4 &c, i16x4 &d) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt field");
   asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "n"(N));
 }
 
