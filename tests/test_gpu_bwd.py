@@ -114,6 +114,31 @@ def test_backward_rows_without_keys(dtype, d, Nq, Nkv):
     _say(f"bwd rows without keys {dtype} d{d}", " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
 
 
+def test_backward_strided_bshd_views():
+    # inputs and outputs stored [B, N, H, d] and passed as [B, H, N, d] views
+    B, H, Nq, Nkv, d = 2, 3, 170, 230, 64
+    w = Workload("bwdv", B, H, Nq, d, "bf16", 9700, tangent_scale=0.1, n_kv=Nkv)
+    x = make_inputs(w)
+    bshd = lambda t: t.transpose(1, 2).contiguous().cuda().transpose(1, 2)
+    q, k, v = (bshd(x[n]) for n in ("q", "k", "v"))
+    assert q.stride() == (Nq * H * d, d, H * d, 1)
+    o, _, lse, _ = aj.fwd(*(bshd(x[n]) for n in NAMES))
+    o = bshd(o.cpu())
+    g_cpu = _grad_input(w, 77)
+    go = bshd(g_cpu)
+    out = (bshd(torch.zeros_like(x["q"])), bshd(torch.zeros_like(x["k"])),
+           bshd(torch.zeros_like(x["v"])), torch.empty((B, H, Nq), device="cuda"))
+    gq, gk, gv, delta = aj.bwd(q, k, v, o, go, lse, out=out)
+    torch.cuda.synchronize()
+    assert gq.stride() == q.stride() and gk.stride() == k.stride()
+    ref = attention_backward(to_float64(x["q"]), to_float64(x["k"]), to_float64(x["v"]),
+                             to_float64(g_cpu))
+    errs = {n: _err(to_float64(a), r) for n, a, r in zip(("dQ", "dK", "dV"), (gq, gk, gv), ref)}
+    for n, e in errs.items():
+        assert e <= TOL["bf16"], f"bshd {n} normwise error {e:.3e}"
+    _say("bwd bshd", " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+
+
 def test_backward_deterministic():
     w = Workload("bwdd", 1, 2, 500, 128, "bf16", 9400, tangent_scale=0.1, n_kv=700)
     x = make_inputs(w)

@@ -82,6 +82,24 @@ def test_splitkv_frame_window():
         _compare([to_float64(t) for t in (o, do, lse, dlse)], ref, "bf16", f"splitkv mask ns{ns}")
 
 
+def test_splitkv_strided_views():
+    # inputs and outputs stored [B, N, H, d] and passed as [B, H, N, d] views
+    B, H, Lq, Lkv, d = 1, 3, 90, 2500, 128
+    w = Workload("skv", B, H, Lq, d, "bf16", 8600, tangent_scale=0.1, n_kv=Lkv)
+    x = make_inputs(w)
+    bshd = lambda t: t.transpose(1, 2).contiguous().cuda().transpose(1, 2)
+    g = [bshd(x[n]) for n in NAMES]
+    o = bshd(torch.zeros((B, H, Lq, d), dtype=torch.bfloat16))
+    do = bshd(torch.zeros((B, H, Lq, d), dtype=torch.bfloat16))
+    lse = torch.empty((B, H, Lq), device="cuda")
+    dlse = torch.empty_like(lse)
+    _, _, _, _, ns = aj.fwd_splitkv(*g, num_splits=5, out=(o, do, lse, dlse))
+    torch.cuda.synchronize()
+    assert ns == 5 and o.stride() == (Lq * H * d, d, H * d, 1)
+    ref = attention_jvp(*(to_float64(x[n]) for n in NAMES))
+    _compare([to_float64(t) for t in (o, do, lse, dlse)], ref, "bf16", "splitkv bshd")
+
+
 def test_one_split_is_fwd_ex_bitwise():
     w = Workload("sk1", 1, 2, 200, 128, "bf16", 8200, tangent_scale=0.1, n_kv=700)
     x = make_inputs(w)
