@@ -9,8 +9,8 @@ d_v) per (batch, head): the six products of the definition (QK^T, dQ K^T,
 Q dK^T over d_qk; P V, P dV, (P . dS) V over d_v), 12 N^2 d when square.
 
 ``--shape B,H,Lq,Lkv,d_qk,d_v`` times a synthetic shape instead of a named
-workload (Gaussian inputs, tangents x 0.1); ``--splitkv S`` times the
-split-KV path (attn_jvp_fwd_splitkv with S splits, 0 = the library's
+workload (Gaussian inputs, tangents x 0.1; ``--dtype fp32`` for float32);
+``--splitkv S`` times the split-KV path (attn_jvp_fwd_splitkv with S splits, 0 = the library's
 choice; the workspace is allocated once, outside the timed region);
 ``--backward`` times the primal backward (attn_jvp_bwd) instead, on O and
 LSE from one forward call and a Gaussian dL/dO, counting the algorithmic
@@ -155,6 +155,8 @@ def main():
     ap.add_argument("--workload", default="image_dit_4096")
     ap.add_argument("--shape", default=None, metavar="B,H,Lq,Lkv,DQK,DV",
                     help="time this synthetic shape instead of a named workload")
+    ap.add_argument("--dtype", default="bf16", choices=("bf16", "fp32"),
+                    help="element type of a --shape workload")
     ap.add_argument("--splitkv", type=int, default=-1, metavar="S",
                     help="time attn_jvp_fwd_splitkv with S key splits (0 = library choice)")
     ap.add_argument("--flush", action="store_true",
@@ -192,7 +194,7 @@ def main():
 
     if args.shape:
         B, H, Lq, Lkv, dqk, dv = (int(t) for t in args.shape.split(","))
-        w = Workload(f"shape_{B}x{H}x{Lq}x{Lkv}x{dqk}x{dv}", B, H, Lq, dqk, "bf16", 1,
+        w = Workload(f"shape_{B}x{H}x{Lq}x{Lkv}x{dqk}x{dv}", B, H, Lq, dqk, args.dtype, 1,
                      tangent_scale=0.1, n_kv=Lkv, d_v=dv)
     else:
         w = WORKLOADS[args.workload]
