@@ -53,6 +53,8 @@ def _vis(mask):
     ("bf16", 2, 1, 37, 2100, 64, 64, 7),
     ("bf16", 1, 1, 130, 1000, 256, 64, 3),
     ("bf16", 1, 2, 64, 300, 128, 128, 64),      # more splits than key tiles
+    ("bf16", 2, 3, 1, 3000, 128, 128, 0),       # one query row
+    ("bf16", 1, 2, 50, 1, 64, 64, 4),           # one key, more splits than tiles
     ("fp32", 1, 2, 64, 1500, 64, 32, 4),
 ])
 def test_splitkv_matches_oracle(dtype, B, H, Lq, Lkv, d, dv, splits):
