@@ -118,10 +118,11 @@ def load():
                                                   i32, vp, sz, vp]
     lib.attn_jvp_fwd_splitkv.restype = i32
     lib.attn_jvp_bwd.argtypes = [vp] * 10 + [ctypes.POINTER(Shape), f32, i32,
-                                             ctypes.POINTER(BwdLayout), vp]
+                                             ctypes.POINTER(BwdLayout), ctypes.POINTER(Mask), vp]
     lib.attn_jvp_bwd.restype = i32
     lib.attn_jvp_bwd_check.argtypes = [vp] * 10 + [ctypes.POINTER(Shape), i32,
-                                                   ctypes.POINTER(BwdLayout)]
+                                                   ctypes.POINTER(BwdLayout),
+                                                   ctypes.POINTER(Mask)]
     lib.attn_jvp_bwd_check.restype = i32
     lib.attn_jvp_tile_shape.argtypes = [i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.attn_jvp_tile_shape.restype = i32
@@ -216,16 +217,17 @@ def attn_jvp_fwd_splitkv(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, shape, scale, dt
 
 
 def attn_jvp_bwd(Q, K, V, O, gO, LSE, gQ, gK, gV, delta, shape, scale, dtype, layout=None,
-                 stream=None):
+                 mask=None, stream=None):
     lay = None if layout is None else ctypes.byref(layout)
     return load().attn_jvp_bwd(Q, K, V, O, gO, LSE, gQ, gK, gV, delta, ctypes.byref(shape),
-                               scale, dtype, lay, stream)
+                               scale, dtype, lay, _mask_ptr(mask), stream)
 
 
-def attn_jvp_bwd_check(Q, K, V, O, gO, LSE, gQ, gK, gV, delta, shape, dtype, layout=None):
+def attn_jvp_bwd_check(Q, K, V, O, gO, LSE, gQ, gK, gV, delta, shape, dtype, layout=None,
+                       mask=None):
     lay = None if layout is None else ctypes.byref(layout)
     return load().attn_jvp_bwd_check(Q, K, V, O, gO, LSE, gQ, gK, gV, delta,
-                                     ctypes.byref(shape), dtype, lay)
+                                     ctypes.byref(shape), dtype, lay, _mask_ptr(mask))
 
 
 def attn_jvp_tile_shape_ex(dtype, d_qk, d_v):
@@ -420,12 +422,14 @@ def fwd_splitkv(q, k, v, dq, dk, dv, scale=None, mask=None, num_splits=0, worksp
     return o, do, lse, dlse, ns
 
 
-def bwd(q, k, v, o, go, lse, scale=None, out=None):
+def bwd(q, k, v, o, go, lse, scale=None, mask=None, out=None):
     """Primal gradients (gq, gk, gv, delta) of a loss with dL/dO = go, for
     q [B, H, Lq, d], k, v [B, H, Lkv, d], o, go [B, H, Lq, d] (bf16 or
     float32) and the forward's lse [B, H, Lq] (float32).  delta is
-    rowsum(go * o).  Outputs are allocated contiguous unless
-    ``out = (gq, gk, gv, delta)`` is given.  Runs on the current stream."""
+    rowsum(go * o).  ``mask`` (as for ``fwd``) gives the gradients of the
+    masked attention; o and lse must come from the forward with the same
+    mask.  Outputs are allocated contiguous unless ``out = (gq, gk, gv,
+    delta)`` is given.  Runs on the current stream."""
     import torch
     dtypes = {torch.bfloat16: ATTN_JVP_BF16, torch.float32: ATTN_JVP_FP32}
     if q.dtype not in dtypes:
@@ -452,7 +456,7 @@ def bwd(q, k, v, o, go, lse, scale=None, out=None):
     st = attn_jvp_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), go.data_ptr(),
                       lse.data_ptr(), gq.data_ptr(), gk.data_ptr(), gv.data_ptr(),
                       delta.data_ptr(), shape, 0.0 if scale is None else float(scale),
-                      dtypes[q.dtype], lay, torch.cuda.current_stream(q.device).cuda_stream)
+                      dtypes[q.dtype], lay, mask, torch.cuda.current_stream(q.device).cuda_stream)
     if st != 0:
         raise AttnJvpError(st, "attn_jvp_bwd")
     return gq, gk, gv, delta

@@ -290,7 +290,8 @@ attn_jvp_bwd_layout contiguous_bwd(const attn_jvp_shape &s) {
 
 int check_bwd(const void *Q, const void *K, const void *V, const void *O, const void *gO,
               const float *LSE, void *gQ, void *gK, void *gV, float *delta,
-              const attn_jvp_shape *shape, int dtype, const attn_jvp_bwd_layout *L) {
+              const attn_jvp_shape *shape, int dtype, const attn_jvp_bwd_layout *L,
+              const attn_jvp_mask *mask) {
   if (!Q || !K || !V || !O || !gO || !LSE || !gQ || !gK || !gV || !delta || !shape || !L)
     return ATTN_JVP_EINVAL;
   const int B = shape->batch, H = shape->heads, Nq = shape->seqlen_q, Nkv = shape->seqlen_kv;
@@ -335,7 +336,7 @@ int check_bwd(const void *Q, const void *K, const void *V, const void *O, const 
     for (int j = i + 1; j < 4; ++j)
       if (overlaps(out[i], out[j])) return ATTN_JVP_ESTRIDE;
   }
-  return ATTN_JVP_OK;
+  return check_mask(mask, Nq, Nkv);
 }
 
 attn_jvp_shape square(int B, int H, int N, int d) {
@@ -513,19 +514,20 @@ int attn_jvp_fwd_splitkv(const void *Q, const void *K, const void *V, const void
 int attn_jvp_bwd_check(const void *Q, const void *K, const void *V, const void *O,
                        const void *gO, const float *LSE, void *gQ, void *gK, void *gV,
                        float *delta, const attn_jvp_shape *shape, int dtype,
-                       const attn_jvp_bwd_layout *layout) {
+                       const attn_jvp_bwd_layout *layout, const attn_jvp_mask *mask) {
   if (!shape) return ATTN_JVP_EINVAL;
   const attn_jvp_bwd_layout L = layout ? *layout : contiguous_bwd(*shape);
-  return check_bwd(Q, K, V, O, gO, LSE, gQ, gK, gV, delta, shape, dtype, &L);
+  return check_bwd(Q, K, V, O, gO, LSE, gQ, gK, gV, delta, shape, dtype, &L, mask);
 }
 
 int attn_jvp_bwd(const void *Q, const void *K, const void *V, const void *O, const void *gO,
                  const float *LSE, void *gQ, void *gK, void *gV, float *delta,
                  const attn_jvp_shape *shape, float scale, int dtype,
-                 const attn_jvp_bwd_layout *layout, void *stream) {
+                 const attn_jvp_bwd_layout *layout, const attn_jvp_mask *mask,
+                 void *stream) {
   if (!shape) return ATTN_JVP_EINVAL;
   const attn_jvp_bwd_layout L = layout ? *layout : contiguous_bwd(*shape);
-  const int st = check_bwd(Q, K, V, O, gO, LSE, gQ, gK, gV, delta, shape, dtype, &L);
+  const int st = check_bwd(Q, K, V, O, gO, LSE, gQ, gK, gV, delta, shape, dtype, &L, mask);
   if (st != ATTN_JVP_OK) return st;
   int bq, bk;
   attn_jvp::bwd_shape_for(dtype == ATTN_JVP_BF16, shape->head_dim_qk, &bq, &bk);
@@ -545,6 +547,7 @@ int attn_jvp_bwd(const void *Q, const void *K, const void *V, const void *O, con
   p.nkb = (p.Nkv + bk - 1) / bk;
   p.scale = (scale > 0.f && isfinite(scale)) ? scale : 1.0f / sqrtf((float)shape->head_dim_qk);
   p.scale_log2 = p.scale * 1.4426950408889634f;
+  p.mask = to_dev(mask);
   const hipError_t err = attn_jvp::launch_bwd(p, dtype == ATTN_JVP_BF16, shape->head_dim_qk,
                                               (hipStream_t)stream);
   return err == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_EHIP;

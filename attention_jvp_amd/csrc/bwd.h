@@ -23,6 +23,13 @@
 // rows past the end and for rows with no visible key, which makes P = 0) and
 // -D from LDS rows that two waves transform once per tile, a tile ahead of
 // use; the dQ kernel masks keys past the end only in the last tile.
+//
+// With the frame-window mask (page "VDN-Minimax-H3 ... Stage A1", yfxerp.com)
+// each launch walks only the streamed tiles its block can see -- key tiles for
+// a query block, as in the forward, and for a key block the query tiles that
+// see it (anchor keys are seen by every query; with anchor_queries_see_all the
+// anchor query frames see every key) -- and applies element masks (P = 0) in
+// the tiles that are only partly visible.
 
 #pragma once
 
@@ -39,7 +46,52 @@ struct BwdParams {
   int B, H, Nq, Nkv;
   int nqb, nkb;                    // query / key blocks per (b, h)
   float scale, scale_log2;
+  MaskDev mask;                    // frame window (kind 0: none); Nq == Nkv when on
 };
+
+// Query-tile ranges [lo, hi) that see some key of rows [k_lo, k_hi) under the
+// frame window: the transpose of visible_tiles.  A block holding a key of an
+// anchor frame is seen by every query; otherwise the queries of the chunks
+// within the radius of the block's chunks, plus (anchor_queries_see_all) the
+// anchor query frames.
+__host__ __device__ inline TileRanges visible_query_tiles(const MaskDev &m, int k_lo, int k_hi,
+                                                          int N, int BN) {
+  TileRanges tr;
+  const int ntiles = (N + BN - 1) / BN;
+  tr.n = 1;
+  tr.lo[0] = 0;
+  tr.hi[0] = ntiles;
+  tr.lo[1] = tr.hi[1] = tr.lo[2] = tr.hi[2] = 0;
+  if (m.kind == 0) return tr;
+  const int T = m.tpf, C = m.chunk, F = m.frames, R = m.radius;
+  const int kf0 = k_lo / T, kf1 = (k_hi - 1) / T;
+  if ((m.first && kf0 == 0) || (m.last && kf1 == F - 1)) return tr;
+  const int c0 = kf0 / C, c1 = kf1 / C;
+  const long long f_lo_l = (long long)(c0 - R) * C;
+  const int f_lo = f_lo_l < 0 ? 0 : (int)f_lo_l;
+  const long long f_hi_l = (long long)(c1 + R + 1) * C;
+  const int f_hi = f_hi_l > F ? F : (int)f_hi_l;
+  tr.n = 0;
+  tr.lo[0] = tr.hi[0] = 0;
+  const bool valid[3] = {m.see_all && m.first, true, m.see_all && m.last};
+  const int a_[3] = {0, f_lo * T / BN, (F - 1) * T / BN};
+  const int z_[3] = {(T + BN - 1) / BN, (f_hi * T + BN - 1) / BN, (F * T + BN - 1) / BN};
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    if (!valid[i]) continue;
+    const int a = a_[i], z = z_[i];
+    if (tr.n == 0) {
+      tr.lo[0] = a; tr.hi[0] = z; tr.n = 1;
+    } else if (tr.n == 1) {
+      if (a <= tr.hi[0]) tr.hi[0] = z > tr.hi[0] ? z : tr.hi[0];
+      else { tr.lo[1] = a; tr.hi[1] = z; tr.n = 2; }
+    } else {
+      if (a <= tr.hi[1]) tr.hi[1] = z > tr.hi[1] ? z : tr.hi[1];
+      else { tr.lo[2] = a; tr.hi[2] = z; tr.n = 3; }
+    }
+  }
+  return tr;
+}
 
 // Global->LDS copies of the streamed tiles: SideCopier's scheme (1 KiB per
 // wave instruction, lane-chosen swizzled chunk, clamped tail rows) for two
@@ -125,7 +177,7 @@ struct BwdCfg {
   static constexpr int kLds = 4 * kBN * RB;                         // 2 stages x 2 tensors
 };
 
-template <typename T, int D, bool KEYS>
+template <typename T, int D, bool KEYS, bool MASKED>
 __global__ __launch_bounds__((64 * (KEYS ? BwdCfg<T, D>::kWavesDkv : BwdCfg<T, D>::kWavesDq)), 1)
 void bwd_kernel(BwdParams p) {
   using C = BwdCfg<T, D>;
@@ -187,7 +239,75 @@ void bwd_kernel(BwdParams p) {
   const int r0 = blk * (W * kWaveRows);
   const int row = r0 + wave * kWaveRows + rl;     // owned row of this lane
   const bool rvalid = row < Nown;
-  const int ntile = (Nstr + BN - 1) / BN;
+  const int r_hi = r0 + W * kWaveRows < Nown ? r0 + W * kWaveRows : Nown;
+
+  // streamed tiles this block visits, in ascending order (all of them
+  // without a mask); iteration it walks tile tile_at(tr, it)
+  TileRanges tr;
+  if constexpr (MASKED) {
+    tr = KEYS ? visible_query_tiles(p.mask, r0, r_hi, Nq, BN)
+              : visible_tiles(p.mask, r0, r_hi, Nkv, BN);
+  } else {
+    tr.n = 1;
+    tr.lo[0] = 0;
+    tr.hi[0] = (Nstr + BN - 1) / BN;
+    tr.lo[1] = tr.hi[1] = tr.lo[2] = tr.hi[2] = 0;
+  }
+  const int ntile = (tr.hi[0] - tr.lo[0]) + (tr.hi[1] - tr.lo[1]) + (tr.hi[2] - tr.lo[2]);
+
+  // Mask terms.  The lane's own row sees the streamed rows [vis_lo, vis_hi)
+  // by the chunk rule, plus [0, a_first_hi) and [a_last_lo, Nstr) (anchor
+  // key frames for the dQ kernel; anchor query frames with
+  // anchor_queries_see_all for the dK/dV kernel; an owned row that is
+  // itself in such a frame sees everything).  Streamed rows in
+  // [win_lo, win_hi) are seen by every row of the block, and so are those
+  // of the anchor intervals, so tiles inside them need no element mask.
+  int vis_lo = 0, vis_hi = Nstr, a_first_hi = 0, a_last_lo = Nstr, win_lo = 0, win_hi = 0;
+  bool blk_all = false;   // dK/dV: every key of the block is an anchor key
+  if constexpr (MASKED) {
+    const long long F = p.mask.frames, TPF = p.mask.tpf, CH = p.mask.chunk, R = p.mask.radius;
+    const int rf = div_fix(rvalid ? row : 0, p.mask.tpf, p.mask.inv_tpf);
+    const int rc = div_fix(rf, p.mask.chunk, p.mask.inv_chunk);
+    const bool r_anchor = (p.mask.first && rf == 0) || (p.mask.last && rf == p.mask.frames - 1);
+    // dQ: an anchor query sees all keys only with see_all; dK/dV: an anchor
+    // key is seen by all queries
+    const bool r_all = KEYS ? r_anchor : (p.mask.see_all && r_anchor);
+    long long flo = (rc - R) * CH, fhi = (rc + R + 1) * CH;
+    flo = flo < 0 ? 0 : flo;
+    fhi = fhi > F ? F : fhi;
+    if (!r_all) {
+      vis_lo = (int)(flo * TPF);
+      vis_hi = fhi > flo ? (int)(fhi * TPF) : vis_lo;
+    }
+    const bool a_on = KEYS ? p.mask.see_all : true;
+    a_first_hi = (a_on && p.mask.first) ? (int)TPF : 0;
+    a_last_lo = (a_on && p.mask.last) ? (int)((F - 1) * TPF) : Nstr;
+    const long long c0 = (r0 / TPF) / CH;
+    const long long c1 = ((r_hi - 1) / TPF) / CH;
+    long long wlo = (c1 - R) * CH, whi = (c0 + R + 1) * CH;
+    wlo = wlo < 0 ? 0 : wlo;
+    whi = whi > F ? F : whi;
+    if (whi > wlo) {
+      win_lo = (int)(wlo * TPF);
+      win_hi = (int)(whi * TPF);
+    }
+    if constexpr (KEYS) {
+      const long long f0 = r0 / TPF, f1 = (r_hi - 1) / TPF;
+      blk_all = (p.mask.first && f1 == 0) || (p.mask.last && f0 == F - 1);
+    }
+  }
+  // does the tile at streamed row t0 need element masks (frame window)?
+  auto needs_mask = [&](int t0) __attribute__((always_inline)) {
+    if constexpr (!MASKED) {
+      return false;
+    } else {
+      const int tz = t0 + BN < Nstr ? t0 + BN : Nstr;
+      const bool in_win = t0 >= win_lo && tz <= win_hi;
+      const bool in_first = tz <= a_first_hi;
+      const bool in_last = t0 >= a_last_lo;
+      return !(blk_all || in_win || in_first || in_last);
+    }
+  };
 
   // streamed tiles: both tensors have rows of D elements, one copier; the
   // same tile is read as operand rows and through transposing loads, so
@@ -203,7 +323,7 @@ void bwd_kernel(BwdParams p) {
   const uint32_t rows_a = lds_addr(smem) + C::kLds;
   auto issue_rows = [&](int it) __attribute__((always_inline)) {
     if constexpr (KEYS) {
-      int qr = it * BN + lane;
+      int qr = tile_at(tr, it) * BN + lane;
       qr = qr < Nq ? qr : Nq - 1;
       const int which = wave < 2 ? wave : 2;
       const float *src = (which == 1 ? DEL : LSE) + qr;
@@ -218,7 +338,7 @@ void bwd_kernel(BwdParams p) {
         const uint32_t a = rows_a + (it % 3) * kRowSlot + wave * 256 + lane * 4;
         float v;
         asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a));
-        const int qr = it * BN + lane;
+        const int qr = tile_at(tr, it) * BN + lane;
         float t;
         if (wave == 0) t = (qr < Nq && v != -INFINITY) ? -v * kLog2e : -INFINITY;
         else t = -v;
@@ -227,14 +347,16 @@ void bwd_kernel(BwdParams p) {
     }
   };
   auto issue_tile = [&](int it, int g) __attribute__((always_inline)) {
-    copier.issue(it * BN, Nstr, smem + g * TL, 2 * TL);
+    copier.issue(tile_at(tr, it) * BN, Nstr, smem + g * TL, 2 * TL);
   };
-  issue_tile(0, 0);
-  issue_rows(0);
-  if (ntile > 1) issue_rows(1);
-  if constexpr (KEYS) {
-    wait_vmem();
-    transform_rows(0);   // visible to all waves after the first tile's barrier
+  if (ntile > 0) {
+    issue_tile(0, 0);
+    issue_rows(0);
+    if (ntile > 1) issue_rows(1);
+    if constexpr (KEYS) {
+      wait_vmem();
+      transform_rows(0);   // visible to all waves after the first tile's barrier
+    }
   }
 
   // owned fragments (B operands): lane holds row rl, d-slice s KI + lg KL
@@ -310,8 +432,9 @@ void bwd_kernel(BwdParams p) {
   //  dK/dV kernel: X = Q K^T (queries x keys), Y = G V^T - D; lane: key rl,
   //               queries 4 lg + i (+16)
   // rows: LDS address of the tile's query-term slot (dK/dV kernel); tail:
-  // the tile holds streamed rows past the end (dQ kernel masks those keys)
-  auto step = [&](auto G_, auto KC_, int t0, uint32_t rows, bool tail)
+  // the tile holds streamed rows past the end (dQ kernel masks those keys);
+  // need: the tile is partly visible under the frame window
+  auto step = [&](auto G_, auto KC_, int t0, uint32_t rows, bool tail, bool need)
                   __attribute__((always_inline)) {
     constexpr int G = decltype(G_)::value;
     constexpr int kb = decltype(KC_)::value * CK;
@@ -390,6 +513,21 @@ void bwd_kernel(BwdParams p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             pv[kb2][i] = sbase + 16 * kb2 + 4 * lg + i < Nkv ? pv[kb2][i] : 0.f;
+      }
+    }
+    if constexpr (MASKED) {
+      if (need) {
+        // bitwise, not short-circuit: no branch per element
+        const int sbase = t0 + kb;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int sr = sbase + 16 * kb2 + 4 * lg + i;
+            const bool in_chunks = (unsigned)(sr - vis_lo) < (unsigned)(vis_hi - vis_lo);
+            const bool vis = in_chunks | (sr < a_first_hi) | (sr >= a_last_lo);
+            pv[kb2][i] = vis ? pv[kb2][i] : 0.f;
+          }
       }
     }
 #pragma unroll
@@ -471,9 +609,11 @@ void bwd_kernel(BwdParams p) {
       if (it + 1 < ntile) transform_rows(it + 1);
     }
     const uint32_t rows = rows_a + (it % 3) * kRowSlot;
-    const bool tail = (it + 1) * BN > Nstr;
+    const int t0 = tile_at(tr, it) * BN;
+    const bool tail = t0 + BN > Nstr;
+    const bool need = needs_mask(t0);
     static_for<0, NSTEP>([&](auto kc) __attribute__((always_inline)) {
-      step(G_, kc, it * BN, rows, tail);
+      step(G_, kc, t0, rows, tail, need);
     });
   };
 
@@ -510,16 +650,21 @@ void bwd_kernel(BwdParams p) {
 }
 
 // dQ (and D) first, then dK and dV, on one stream.
-template <typename T, int D>
-hipError_t launch_bwd_instance(const BwdParams &p, hipStream_t s) {
+template <typename T, int D, bool MASKED>
+hipError_t launch_bwd_pair(const BwdParams &p, hipStream_t s) {
   using C = BwdCfg<T, D>;
-  hipLaunchKernelGGL((bwd_kernel<T, D, false>), dim3(p.B * p.H * p.nqb), dim3(64 * C::kWavesDq),
-                     0, s, p);
+  hipLaunchKernelGGL((bwd_kernel<T, D, false, MASKED>), dim3(p.B * p.H * p.nqb),
+                     dim3(64 * C::kWavesDq), 0, s, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((bwd_kernel<T, D, true>), dim3(p.B * p.H * p.nkb), dim3(64 * C::kWavesDkv),
-                     0, s, p);
+  hipLaunchKernelGGL((bwd_kernel<T, D, true, MASKED>), dim3(p.B * p.H * p.nkb),
+                     dim3(64 * C::kWavesDkv), 0, s, p);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_bwd_instance(const BwdParams &p, hipStream_t s) {
+  return p.mask.kind != 0 ? launch_bwd_pair<T, D, true>(p, s) : launch_bwd_pair<T, D, false>(p, s);
 }
 
 }  // namespace attn_jvp

@@ -12,10 +12,11 @@ Q dK^T over d_qk; P V, P dV, (P . dS) V over d_v), 12 N^2 d when square.
 workload (Gaussian inputs, tangents x 0.1; ``--dtype fp32`` for float32);
 ``--splitkv S`` times the split-KV path (attn_jvp_fwd_splitkv with S splits, 0 = the library's
 choice; the workspace is allocated once, outside the timed region);
-``--backward`` times the primal backward (attn_jvp_bwd) instead, on O and
-LSE from one forward call and a Gaussian dL/dO, counting the algorithmic
-10 * Lq * Lkv * d FLOPs per (batch, head) (S, dP, dV, dK, dQ; the
-recomputation of S and dP in the second launch is not counted).
+``--backward`` times the primal backward (attn_jvp_bwd, with the workload's
+mask if it has one) instead, on O and LSE from one forward call and a
+Gaussian dL/dO, counting the algorithmic 10 * (visible pairs) * d FLOPs per
+(batch, head) (S, dP, dV, dK, dQ; the recomputation of S and dP in the
+second launch is not counted).
 
 The warm-up runs at least ``--warmup`` steps and at least 0.3 s of work, so
 the timed steps run at the sustained engine clock (``warmup_run`` in the
@@ -216,17 +217,17 @@ def main():
         log(f"split-KV: {splits} splits, workspace {need} bytes")
 
     if args.backward:
-        if mask is not None or splits is not None or w.dv != w.d:
-            print("--backward: dense, one head dim, no split-KV", file=sys.stderr)
+        if splits is not None or w.dv != w.d:
+            print("--backward: one head dim, no split-KV", file=sys.stderr)
             sys.exit(2)
-        aj.fwd(*g, out=outs)
+        aj.fwd(*g, mask=mask, out=outs)
         go = torch.randn(o.shape, generator=torch.Generator().manual_seed(7)).to(o.dtype).cuda()
         grads = (torch.empty_like(g[0]), torch.empty_like(g[1]), torch.empty_like(g[2]),
                  torch.empty_like(lse))
 
     def step():
         if args.backward:
-            aj.bwd(g[0], g[1], g[2], o, go, lse, out=grads)
+            aj.bwd(g[0], g[1], g[2], o, go, lse, mask=mask, out=grads)
         elif splits is None:
             aj.fwd(*g, mask=mask, out=outs)
         else:

@@ -208,7 +208,11 @@ int attn_jvp_fwd_splitkv(const void *Q, const void *K, const void *V,
  *   gQ = s dS K,              gK = s dS^T Q.
  * The tangents play no part (they are not trained).  As on the pages, the
  * backward is built for d_qk == d_v only (otherwise ATTN_JVP_EUNSUPPORTED);
- * Lq may differ from Lkv.  No mask. */
+ * Lq may differ from Lkv.  An optional frame-window mask (the forward's
+ * attn_jvp_mask, same rules: Lq == Lkv == frames * tokens_per_frame) gives
+ * the gradients of the masked attention: P = 0 for every pair the window
+ * hides (page "VDN-Minimax-H3 ... Stage A1"); pass the LSE and O of the
+ * forward with the same mask. */
 
 /* Element strides (batch, head, row) of the backward's tensors. */
 typedef struct {
@@ -219,20 +223,24 @@ typedef struct {
 /* gQ [B,H,Lq,d], gK, gV [B,H,Lkv,d] (the dtype) from Q, K, V, O, gO (the
  * dtype) and LSE (float32 [B,H,Lq], as the forward wrote it).  delta is a
  * caller-owned float32 [B,H,Lq] buffer that receives D = rowsum(gO (.) O).
- * `layout` NULL means every tensor contiguous in its shape.  scale <= 0
- * selects 1/sqrt(d).  Two launches on `stream` (dQ and D, then dK and dV);
- * deterministic (no atomics).  Outputs must not overlap inputs or each
- * other.  Returns a status; nothing is launched unless it is ATTN_JVP_OK. */
+ * `layout` NULL means every tensor contiguous in its shape; `mask` NULL (or
+ * kind ATTN_JVP_MASK_NONE) means dense.  scale <= 0 selects 1/sqrt(d).  Two
+ * launches on `stream` (dQ and D, then dK and dV); deterministic (no
+ * atomics).  Outputs must not overlap inputs or each other.  Returns a
+ * status (ATTN_JVP_EMASK for a mask the forward would reject); nothing is
+ * launched unless it is ATTN_JVP_OK. */
 int attn_jvp_bwd(const void *Q, const void *K, const void *V, const void *O,
                  const void *gO, const float *LSE, void *gQ, void *gK, void *gV,
                  float *delta, const attn_jvp_shape *shape, float scale, int dtype,
-                 const attn_jvp_bwd_layout *layout, void *stream);
+                 const attn_jvp_bwd_layout *layout, const attn_jvp_mask *mask,
+                 void *stream);
 
 /* Host-only argument check of attn_jvp_bwd (never touches the GPU). */
 int attn_jvp_bwd_check(const void *Q, const void *K, const void *V, const void *O,
                        const void *gO, const float *LSE, void *gQ, void *gK,
                        void *gV, float *delta, const attn_jvp_shape *shape,
-                       int dtype, const attn_jvp_bwd_layout *layout);
+                       int dtype, const attn_jvp_bwd_layout *layout,
+                       const attn_jvp_mask *mask);
 
 /* Contiguous [B, H, N, d] tensors.  scale <= 0 selects 1/sqrt(d).
  * Returns an attn_jvp_status. */

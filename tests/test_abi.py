@@ -264,3 +264,12 @@ def test_bwd_check():
     q = list(p)
     q[9] = p[5]                                     # delta overlaps LSE
     assert aj.attn_jvp_bwd_check(*q, shape, 0) == -3
+    # frame-window mask: the forward's rules (square, frames x tokens = N)
+    win = aj.Mask.frame_window(frames=5, tokens_per_frame=40, chunk_frames=2, radius_chunks=1)
+    ps = _bwd_ptrs(1, 2, 200, 200, 64, 2)
+    sq = aj.Shape(1, 2, 200, 200, 64, 64)
+    assert aj.attn_jvp_bwd_check(*ps, sq, 0, None, win) == 0
+    assert aj.attn_jvp_bwd_check(*_bwd_ptrs(1, 2, 200, 240, 64, 2), aj.Shape(1, 2, 200, 240, 64, 64),
+                                 0, None, win) == -4                          # Lq != Lkv
+    bad = aj.Mask.frame_window(frames=6, tokens_per_frame=40, chunk_frames=2, radius_chunks=1)
+    assert aj.attn_jvp_bwd_check(*ps, sq, 0, None, bad) == -4                 # 240 tokens != 200

@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import attention_jvp_amd as aj
-from oracle import attention_backward, attention_jvp
+from oracle import FrameWindow, attention_backward, attention_jvp
 from synth import Workload, make_inputs, to_float64
 
 pytestmark = pytest.mark.gpu
@@ -150,6 +150,43 @@ def test_backward_strided_bshd_views():
     for n, e in errs.items():
         assert e <= TOL["bf16"], f"bshd {n} normwise error {e:.3e}"
     _say("bwd bshd", " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+
+
+@pytest.mark.parametrize("F,T,C,R,first,last,see_all,dtype,d", [
+    (7, 37, 2, 1, 1, 1, 0, "bf16", 128),
+    (9, 64, 3, 0, 1, 0, 0, "bf16", 64),
+    (6, 50, 2, 0, 0, 1, 1, "bf16", 128),
+    (12, 30, 2, 0, 1, 1, 1, "bf16", 64),     # anchor query frames far from the window
+    (11, 40, 1, 1, 1, 1, 0, "fp32", 64),
+    (5, 100, 5, 0, 0, 0, 0, "bf16", 128),
+    (8, 33, 3, 1, 0, 0, 1, "bf16", 256),
+])
+def test_backward_frame_window(F, T, C, R, first, last, see_all, dtype, d):
+    # masked forward (O, LSE) then the masked backward, against the oracle's
+    # backward of the masked attention
+    N = F * T
+    what = f"bwd mask F{F} T{T} C{C} R{R} a{first}{last}{see_all} {dtype} d{d}"
+    _say(what)
+    mask = dict(frames=F, tokens_per_frame=T, chunk_frames=C, radius_chunks=R,
+                anchor_first=first, anchor_last=last, anchor_queries_see_all=see_all)
+    vis = FrameWindow(frames=F, tokens_per_frame=T, chunk_frames=C, radius_chunks=R,
+                      anchor_first=bool(first), anchor_last=bool(last),
+                      anchor_queries_see_all=bool(see_all))
+    w = Workload("bwdm", 1, 2, N, d, dtype, 9800 + N + d, tangent_scale=0.1)
+    x = make_inputs(w)
+    q, k, v = (x[n].cuda() for n in ("q", "k", "v"))
+    o, _, lse, _ = aj.fwd(*(x[n].cuda() for n in NAMES), mask=mask)
+    g_cpu = _grad_input(w, w.seed + 1)
+    gq, gk, gv, delta = aj.bwd(q, k, v, o, g_cpu.cuda(), lse, mask=mask)
+    torch.cuda.synchronize()
+    ref = attention_backward(to_float64(x["q"]), to_float64(x["k"]), to_float64(x["v"]),
+                             to_float64(g_cpu), visible=vis)
+    floor = float(np.max(np.abs(ref[2])))
+    errs = {}
+    for n, a, r in zip(("dQ", "dK", "dV"), (gq, gk, gv), ref):
+        errs[n] = _err(to_float64(a), r, floor)
+        assert errs[n] <= TOL[dtype], f"{what}: {n} normwise error {errs[n]:.3e}"
+    _say(what, " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
 
 
 def test_backward_deterministic():
