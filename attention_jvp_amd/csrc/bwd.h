@@ -47,6 +47,7 @@ struct BwdParams {
   int nqb, nkb;                    // query / key blocks per (b, h)
   float scale, scale_log2;
   MaskDev mask;                    // frame window (kind 0: none); Nq == Nkv when on
+  int rbq;                         // 16-row blocks per dQ wave (1, or 2 where built)
 };
 
 // Query-tile ranges [lo, hi) that see some key of rows [k_lo, k_hi) under the
@@ -169,6 +170,10 @@ struct BwdCfg {
   static constexpr int kResDq = (ES == 2 ? D / 4 : D / 2) + D / 4;
   static constexpr int kResDkv = (ES == 2 ? D / 4 : D / 2) + D / 2;
   static constexpr int kWavesDq = kResDq <= 96 ? 8 : 4;
+  // bfloat16 d = 128 dQ waves may own two 16-row blocks (the resident set
+  // stays within 128 VGPRs): every streamed LDS fragment then feeds both
+  // blocks, halving the LDS bytes per MFMA of the launch that is LDS-bound
+  static constexpr int kRbDqMax = (ES == 2 && D == 128) ? 2 : 1;
   static constexpr int kWavesDkv = kResDkv <= (ES == 2 ? 96 : 48) ? 8 : 4;
   // 64-row tiles while two stages of both tensors fit in 128 KiB and the
   // transposing reads' largest constant offset (stage, second tensor, row
@@ -177,7 +182,7 @@ struct BwdCfg {
   static constexpr int kLds = 4 * kBN * RB;                         // 2 stages x 2 tensors
 };
 
-template <typename T, int D, bool KEYS, bool MASKED>
+template <typename T, int D, bool KEYS, bool MASKED, int RBQ>
 __global__ __launch_bounds__((64 * (KEYS ? BwdCfg<T, D>::kWavesDkv : BwdCfg<T, D>::kWavesDq)), 1)
 void bwd_kernel(BwdParams p) {
   using C = BwdCfg<T, D>;
@@ -187,6 +192,8 @@ void bwd_kernel(BwdParams p) {
   using FragV = typename EV::Frag;
   constexpr bool BF16 = sizeof(T) == 2;
   constexpr int W = KEYS ? C::kWavesDkv : C::kWavesDq;
+  constexpr int R = KEYS ? 1 : RBQ;   // 16-row blocks per wave
+  static_assert(R >= 1 && R <= C::kRbDqMax, "row blocks");
   constexpr int BN = C::kBN;
   constexpr int CK = kStepKeys;
   constexpr int NSTEP = BN / CK;
@@ -206,7 +213,7 @@ void bwd_kernel(BwdParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rl = lane & 15;       // this lane's owned row (query or key) within the wave
+  const int rl = lane & 15;       // this lane's owned row (query or key) within a row block
   const int lg = lane >> 4;
 
   const int lid = logical_block_id();
@@ -236,10 +243,16 @@ void bwd_kernel(BwdParams p) {
   const float *LSE = p.lse + (int64_t)bh * Nq;
   float *DEL = p.delta + (int64_t)bh * Nq;
 
-  const int r0 = blk * (W * kWaveRows);
-  const int row = r0 + wave * kWaveRows + rl;     // owned row of this lane
-  const bool rvalid = row < Nown;
-  const int r_hi = r0 + W * kWaveRows < Nown ? r0 + W * kWaveRows : Nown;
+  // owned rows of the lane: one per row block, r0 + 16 (R wave + rb) + rl
+  const int r0 = blk * (W * R * kWaveRows);
+  int row[R];
+  bool rvalid[R];
+#pragma unroll
+  for (int rb = 0; rb < R; ++rb) {
+    row[rb] = r0 + (wave * R + rb) * kWaveRows + rl;
+    rvalid[rb] = row[rb] < Nown;
+  }
+  const int r_hi = r0 + W * R * kWaveRows < Nown ? r0 + W * R * kWaveRows : Nown;
 
   // streamed tiles this block visits, in ascending order (all of them
   // without a mask); iteration it walks tile tile_at(tr, it)
@@ -262,29 +275,38 @@ void bwd_kernel(BwdParams p) {
   // itself in such a frame sees everything).  Streamed rows in
   // [win_lo, win_hi) are seen by every row of the block, and so are those
   // of the anchor intervals, so tiles inside them need no element mask.
-  int vis_lo = 0, vis_hi = Nstr, a_first_hi = 0, a_last_lo = Nstr, win_lo = 0, win_hi = 0;
+  int vis_lo[R], vis_hi[R];
+  int a_first_hi = 0, a_last_lo = Nstr, win_lo = 0, win_hi = 0;
   bool blk_all = false;   // dK/dV: every key of the block is an anchor key
+#pragma unroll
+  for (int rb = 0; rb < R; ++rb) {
+    vis_lo[rb] = 0;
+    vis_hi[rb] = Nstr;
+  }
   if constexpr (MASKED) {
-    const long long F = p.mask.frames, TPF = p.mask.tpf, CH = p.mask.chunk, R = p.mask.radius;
-    const int rf = div_fix(rvalid ? row : 0, p.mask.tpf, p.mask.inv_tpf);
-    const int rc = div_fix(rf, p.mask.chunk, p.mask.inv_chunk);
-    const bool r_anchor = (p.mask.first && rf == 0) || (p.mask.last && rf == p.mask.frames - 1);
-    // dQ: an anchor query sees all keys only with see_all; dK/dV: an anchor
-    // key is seen by all queries
-    const bool r_all = KEYS ? r_anchor : (p.mask.see_all && r_anchor);
-    long long flo = (rc - R) * CH, fhi = (rc + R + 1) * CH;
-    flo = flo < 0 ? 0 : flo;
-    fhi = fhi > F ? F : fhi;
-    if (!r_all) {
-      vis_lo = (int)(flo * TPF);
-      vis_hi = fhi > flo ? (int)(fhi * TPF) : vis_lo;
+    const long long F = p.mask.frames, TPF = p.mask.tpf, CH = p.mask.chunk, Rd = p.mask.radius;
+#pragma unroll
+    for (int rb = 0; rb < R; ++rb) {
+      const int rf = div_fix(rvalid[rb] ? row[rb] : 0, p.mask.tpf, p.mask.inv_tpf);
+      const int rc = div_fix(rf, p.mask.chunk, p.mask.inv_chunk);
+      const bool r_anchor = (p.mask.first && rf == 0) || (p.mask.last && rf == p.mask.frames - 1);
+      // dQ: an anchor query sees all keys only with see_all; dK/dV: an
+      // anchor key is seen by all queries
+      const bool r_all = KEYS ? r_anchor : (p.mask.see_all && r_anchor);
+      long long flo = (rc - Rd) * CH, fhi = (rc + Rd + 1) * CH;
+      flo = flo < 0 ? 0 : flo;
+      fhi = fhi > F ? F : fhi;
+      if (!r_all) {
+        vis_lo[rb] = (int)(flo * TPF);
+        vis_hi[rb] = fhi > flo ? (int)(fhi * TPF) : vis_lo[rb];
+      }
     }
     const bool a_on = KEYS ? p.mask.see_all : true;
     a_first_hi = (a_on && p.mask.first) ? (int)TPF : 0;
     a_last_lo = (a_on && p.mask.last) ? (int)((F - 1) * TPF) : Nstr;
     const long long c0 = (r0 / TPF) / CH;
     const long long c1 = ((r_hi - 1) / TPF) / CH;
-    long long wlo = (c1 - R) * CH, whi = (c0 + R + 1) * CH;
+    long long wlo = (c1 - Rd) * CH, whi = (c0 + Rd + 1) * CH;
     wlo = wlo < 0 ? 0 : wlo;
     whi = whi > F ? F : whi;
     if (whi > wlo) {
@@ -359,50 +381,60 @@ void bwd_kernel(BwdParams p) {
     }
   }
 
-  // owned fragments (B operands): lane holds row rl, d-slice s KI + lg KL
-  FragK af[DS], bf[DS];
+  // owned fragments (B operands): lane holds row rl of each row block,
+  // d-slice s KI + lg KL
+  FragK af[R][DS], bf[R][DS];
 #pragma unroll
-  for (int s = 0; s < DS; ++s) {
-    if (rvalid) {
-      af[s] = *(const FragK *)(A0 + (int64_t)row * as0 + s * KI + lg * KL);
-      bf[s] = *(const FragK *)(A1 + (int64_t)row * as1 + s * KI + lg * KL);
-    } else {
-      af[s] = FragK{};
-      bf[s] = FragK{};
+  for (int rb = 0; rb < R; ++rb)
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      if (rvalid[rb]) {
+        af[rb][s] = *(const FragK *)(A0 + (int64_t)row[rb] * as0 + s * KI + lg * KL);
+        bf[rb][s] = *(const FragK *)(A1 + (int64_t)row[rb] * as1 + s * KI + lg * KL);
+      } else {
+        af[rb][s] = FragK{};
+        bf[rb][s] = FragK{};
+      }
     }
-  }
 
   // dQ kernel: the lane's query row terms.  D = rowsum(G (.) O) from the
   // lane's quarter of the row (the same d-slices as its G fragments),
   // summed over the row's four lanes; L2 = LSE * log2 e (+inf for a row
   // with no visible key, so that P = 0 there).
-  float d_row = 0.f, l2_row = 0.f;
-  if constexpr (!KEYS) {
-    const T *Orow = (const T *)p.o + b * p.so[0] + h * p.so[1];
-    float part = 0.f;
-    if (rvalid) {
+  float d_row[R], l2_row[R];
 #pragma unroll
-      for (int s = 0; s < DS; ++s) {
-        const FragK of = *(const FragK *)(Orow + (int64_t)row * p.so[2] + s * KI + lg * KL);
-        if constexpr (BF16) {
+  for (int rb = 0; rb < R; ++rb) {
+    d_row[rb] = 0.f;
+    l2_row[rb] = 0.f;
+    if constexpr (!KEYS) {
+      const T *Orow = (const T *)p.o + b * p.so[0] + h * p.so[1];
+      float part = 0.f;
+      if (rvalid[rb]) {
 #pragma unroll
-          for (int j = 0; j < KL; ++j) part = fmaf((float)bf[s][j], (float)of[j], part);
-        } else {
-          part = fmaf(bf[s], of, part);
+        for (int s = 0; s < DS; ++s) {
+          const FragK of = *(const FragK *)(Orow + (int64_t)row[rb] * p.so[2] + s * KI + lg * KL);
+          if constexpr (BF16) {
+#pragma unroll
+            for (int j = 0; j < KL; ++j) part = fmaf((float)bf[rb][s][j], (float)of[j], part);
+          } else {
+            part = fmaf(bf[rb][s], of, part);
+          }
         }
       }
+      d_row[rb] = row_sum4(part);
+      if (rvalid[rb] && lg == 0) DEL[row[rb]] = d_row[rb];
+      const float lse = rvalid[rb] ? LSE[row[rb]] : 0.f;
+      l2_row[rb] = lse == -INFINITY ? INFINITY : lse * kLog2e;
     }
-    d_row = row_sum4(part);
-    if (rvalid && lg == 0) DEL[row] = d_row;
-    const float lse = rvalid ? LSE[row] : 0.f;
-    l2_row = lse == -INFINITY ? INFINITY : lse * kLog2e;
   }
 
   // accumulators: dQ^T (dQ kernel) or dK^T and dV^T (dK/dV kernel); lane
   // holds d = 16e + 4 lg + 0..3 of its owned row
-  f32x4 acc0[ND], acc1[KEYS ? ND : 1];
+  f32x4 acc0[R][ND], acc1[KEYS ? ND : 1];
 #pragma unroll
-  for (int e = 0; e < ND; ++e) acc0[e] = f32x4{};
+  for (int rb = 0; rb < R; ++rb)
+#pragma unroll
+    for (int e = 0; e < ND; ++e) acc0[rb][e] = f32x4{};
   if constexpr (KEYS) {
 #pragma unroll
     for (int e = 0; e < ND; ++e) acc1[e] = f32x4{};
@@ -423,8 +455,13 @@ void bwd_kernel(BwdParams p) {
 
   // dQ kernel: -LSE log2 e of the lane's query (-inf for a row with no
   // visible key, so that P = 0 there) and the start value of its dP sums
-  const float nl2_row = KEYS ? 0.f : -l2_row;
-  const f32x4 nd_row = f32x4{-d_row, -d_row, -d_row, -d_row};
+  float nl2_row[R];
+  f32x4 nd_row[R];
+#pragma unroll
+  for (int rb = 0; rb < R; ++rb) {
+    nl2_row[rb] = KEYS ? 0.f : -l2_row[rb];
+    nd_row[rb] = f32x4{-d_row[rb], -d_row[rb], -d_row[rb], -d_row[rb]};
+  }
 
   // One 32-row step kc of the streamed tile in stage G.
   //  dQ kernel:   X^T = K Q^T (keys x queries), Y^T = V G^T - D; lane: query
@@ -446,14 +483,12 @@ void bwd_kernel(BwdParams p) {
         nl2[kb2] = lds_read_f4(a);
         y0[kb2] = lds_read_f4(a + 256);
       }
-    } else {
-      y0[0] = nd_row;
-      y0[1] = nd_row;
     }
-    f32x4 xs[2], ys[2];
+    // S (xs) and dP - D (ys) of each row block
+    f32x4 xs[R][2], ys[R][2];
     if constexpr (BF16 && D >= 32) {
-      // slices j = (kb2, s), kb2-major, each a tensor-0 and a tensor-1 read;
-      // PD slices in flight
+      // slices j = (kb2, s), kb2-major, each a tensor-0 and a tensor-1 read
+      // that feed every row block; PD slices in flight
       constexpr int NP = 2 * DS;
       constexpr int PD0 = D >= 128 ? 3 : 2;
       constexpr int PD = PD0 < NP ? PD0 : NP;
@@ -467,52 +502,81 @@ void bwd_kernel(BwdParams p) {
       };
       static_for<0, PD - 1>([&](auto j_) __attribute__((always_inline)) { issue(j_); });
       if constexpr (KEYS) lds_quad_wait<2 * (PD - 1)>(nl2[0], nl2[1], y0[0], y0[1]);
-      f32x4 x_[2] = {f32x4{}, f32x4{}}, y_[2] = {y0[0], y0[1]};
+      f32x4 x_[R][2], y_[R][2];
+#pragma unroll
+      for (int rb = 0; rb < R; ++rb)
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          x_[rb][kb2] = f32x4{};
+          y_[rb][kb2] = KEYS ? y0[kb2] : nd_row[rb];
+        }
       static_for<0, NP>([&](auto j_) __attribute__((always_inline)) {
         constexpr int j = decltype(j_)::value;
         constexpr int kb2 = j / DS, s = j % DS;
         if constexpr (j + PD - 1 < NP) issue(std::integral_constant<int, j + PD - 1>{});
         constexpr int newer = (NP - 1 - j) < (PD - 1) ? (NP - 1 - j) : (PD - 1);
         lds_pair_wait<2 * newer>(r0f[j], r1f[j]);
-        x_[kb2] = EK::mfma(r0f[j], af[s], x_[kb2]);
-        y_[kb2] = EK::mfma(r1f[j], bf[s], y_[kb2]);
+#pragma unroll
+        for (int rb = 0; rb < R; ++rb) {
+          x_[rb][kb2] = EK::mfma(r0f[j], af[rb][s], x_[rb][kb2]);
+          y_[rb][kb2] = EK::mfma(r1f[j], bf[rb][s], y_[rb][kb2]);
+        }
       });
-      xs[0] = x_[0];
-      xs[1] = x_[1];
-      ys[0] = y_[0];
-      ys[1] = y_[1];
+#pragma unroll
+      for (int rb = 0; rb < R; ++rb)
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          xs[rb][kb2] = x_[rb][kb2];
+          ys[rb][kb2] = y_[rb][kb2];
+        }
     } else {
       if constexpr (KEYS) lds_quad_wait<0>(nl2[0], nl2[1], y0[0], y0[1]);
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
-        f32x4 x_ = f32x4{}, y_ = y0[kb2];
+        f32x4 x_[R], y_[R];
+#pragma unroll
+        for (int rb = 0; rb < R; ++rb) {
+          x_[rb] = f32x4{};
+          y_[rb] = KEYS ? y0[kb2] : nd_row[rb];
+        }
 #pragma unroll
         for (int s = 0; s < DS; ++s) {
           const char *rp = smem + (rdl[s] - smem_a) + G * TL + (kb + 16 * kb2) * RB;
           const FragK r0f = *(const FragK *)rp;
           const FragK r1f = *(const FragK *)(rp + 2 * TL);
-          x_ = EK::mfma(r0f, af[s], x_);
-          y_ = EK::mfma(r1f, bf[s], y_);
+#pragma unroll
+          for (int rb = 0; rb < R; ++rb) {
+            x_[rb] = EK::mfma(r0f, af[rb][s], x_[rb]);
+            y_[rb] = EK::mfma(r1f, bf[rb][s], y_[rb]);
+          }
         }
-        xs[kb2] = x_;
-        ys[kb2] = y_;
+#pragma unroll
+        for (int rb = 0; rb < R; ++rb) {
+          xs[rb][kb2] = x_[rb];
+          ys[rb][kb2] = y_[rb];
+        }
       }
     }
     // P and dS = P (.) (dP - D), unscaled
-    f32x4 pv[2], dsv[2];
+    f32x4 pv[R][2], dsv[R][2];
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
+    for (int rb = 0; rb < R; ++rb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        pv[kb2][i] = __builtin_amdgcn_exp2f(fmaf(xs[kb2][i], c2, KEYS ? nl2[kb2][i] : nl2_row));
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          pv[rb][kb2][i] =
+              __builtin_amdgcn_exp2f(fmaf(xs[rb][kb2][i], c2, KEYS ? nl2[kb2][i] : nl2_row[rb]));
     if constexpr (!KEYS) {
       if (tail) {
         const int sbase = t0 + kb;   // first key of the step
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
+        for (int rb = 0; rb < R; ++rb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            pv[kb2][i] = sbase + 16 * kb2 + 4 * lg + i < Nkv ? pv[kb2][i] : 0.f;
+          for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              pv[rb][kb2][i] = sbase + 16 * kb2 + 4 * lg + i < Nkv ? pv[rb][kb2][i] : 0.f;
       }
     }
     if constexpr (MASKED) {
@@ -520,31 +584,41 @@ void bwd_kernel(BwdParams p) {
         // bitwise, not short-circuit: no branch per element
         const int sbase = t0 + kb;
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
+        for (int rb = 0; rb < R; ++rb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int sr = sbase + 16 * kb2 + 4 * lg + i;
-            const bool in_chunks = (unsigned)(sr - vis_lo) < (unsigned)(vis_hi - vis_lo);
-            const bool vis = in_chunks | (sr < a_first_hi) | (sr >= a_last_lo);
-            pv[kb2][i] = vis ? pv[kb2][i] : 0.f;
-          }
+          for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int sr = sbase + 16 * kb2 + 4 * lg + i;
+              const bool in_chunks = (unsigned)(sr - vis_lo[rb]) < (unsigned)(vis_hi[rb] - vis_lo[rb]);
+              const bool vis = in_chunks | (sr < a_first_hi) | (sr >= a_last_lo);
+              pv[rb][kb2][i] = vis ? pv[rb][kb2][i] : 0.f;
+            }
       }
     }
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
+    for (int rb = 0; rb < R; ++rb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dsv[kb2][i] = pv[kb2][i] * ys[kb2][i];
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dsv[rb][kb2][i] = pv[rb][kb2][i] * ys[rb][kb2][i];
     // products over the 32 streamed rows: acc0 += T0^T (dS or P) ; acc1 ...
-    //  dQ kernel:    dQ^T += K^T dS^T        (T0 = K tile, transposed reads)
+    //  dQ kernel:    dQ^T += K^T dS^T        (T0 = K tile, transposed reads,
+    //                                         shared by the row blocks)
     //  dK/dV kernel: dK^T += Q^T dS, dV^T += G^T P
     if constexpr (BF16) {
-      bf16x8 dsf, pf;
+      bf16x8 dsf[R], pf;
+#pragma unroll
+      for (int rb = 0; rb < R; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          dsf[rb][i] = (__bf16)dsv[rb][0][i];
+          dsf[rb][4 + i] = (__bf16)dsv[rb][1][i];
+        }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        dsf[i] = (__bf16)dsv[0][i];
-        dsf[4 + i] = (__bf16)dsv[1][i];
-        pf[i] = (__bf16)pv[0][i];
-        pf[4 + i] = (__bf16)pv[1][i];
+        pf[i] = (__bf16)pv[0][0][i];
+        pf[4 + i] = (__bf16)pv[0][1][i];
       }
       constexpr int VO = G * TL + kb * RB;
       constexpr int NR = KEYS ? 4 : 2;          // transposing reads per d block
@@ -572,7 +646,8 @@ void bwd_kernel(BwdParams p) {
           lds_tr_wait<0>(cur[0], cur[1], cur[2], cur[3]);
         }
         const FragV t0f = __builtin_bit_cast(FragV, __builtin_shufflevector(cur[0], cur[1], 0, 1, 2, 3, 4, 5, 6, 7));
-        acc0[e] = EV::mfma(t0f, dsf, acc0[e]);
+#pragma unroll
+        for (int rb = 0; rb < R; ++rb) acc0[rb][e] = EV::mfma(t0f, dsf[rb], acc0[rb][e]);
         if constexpr (KEYS) {
           const FragV t1f = __builtin_bit_cast(FragV, __builtin_shufflevector(cur[2], cur[3], 0, 1, 2, 3, 4, 5, 6, 7));
           acc1[e] = EV::mfma(t1f, pf, acc1[e]);
@@ -590,10 +665,11 @@ void bwd_kernel(BwdParams p) {
           for (int e = 0; e < ND; ++e) {
             const int o = lds_off<RB, true>(r, (16 * e + rl) * 4);
             const FragV t0f = *(const FragV *)(Ts + o);
-            acc0[e] = EV::mfma(t0f, dsv[kb2][i], acc0[e]);
+#pragma unroll
+            for (int rb = 0; rb < R; ++rb) acc0[rb][e] = EV::mfma(t0f, dsv[rb][kb2][i], acc0[rb][e]);
             if constexpr (KEYS) {
               const FragV t1f = *(const FragV *)(Ts + 2 * TL + o);
-              acc1[e] = EV::mfma(t1f, pv[kb2][i], acc1[e]);
+              acc1[e] = EV::mfma(t1f, pv[0][kb2][i], acc1[e]);
             }
           }
         }
@@ -625,19 +701,21 @@ void bwd_kernel(BwdParams p) {
   if (it < ntile) tile(std::integral_constant<int, 0>{}, it);
 
   // epilogue: dQ = s dQ^T, dK = s dK^T, dV = dV^T
-  if (rvalid) {
-    typedef T T4 __attribute__((ext_vector_type(4)));
-    T *O0 = KEYS ? (T *)p.gk + b * p.sgk[0] + h * p.sgk[1] + (int64_t)row * p.sgk[2]
-                 : (T *)p.gq + b * p.sgq[0] + h * p.sgq[1] + (int64_t)row * p.sgq[2];
+  typedef T T4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int rb = 0; rb < R; ++rb) {
+    if (!rvalid[rb]) continue;
+    T *O0 = KEYS ? (T *)p.gk + b * p.sgk[0] + h * p.sgk[1] + (int64_t)row[rb] * p.sgk[2]
+                 : (T *)p.gq + b * p.sgq[0] + h * p.sgq[1] + (int64_t)row[rb] * p.sgq[2];
 #pragma unroll
     for (int e = 0; e < ND; ++e) {
       T4 o;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = (T)(acc0[e][i] * p.scale);
+      for (int i = 0; i < 4; ++i) o[i] = (T)(acc0[rb][e][i] * p.scale);
       *(T4 *)(O0 + 16 * e + 4 * lg) = o;
     }
     if constexpr (KEYS) {
-      T *O1 = (T *)p.gv + b * p.sgv[0] + h * p.sgv[1] + (int64_t)row * p.sgv[2];
+      T *O1 = (T *)p.gv + b * p.sgv[0] + h * p.sgv[1] + (int64_t)row[rb] * p.sgv[2];
 #pragma unroll
       for (int e = 0; e < ND; ++e) {
         T4 o;
@@ -653,11 +731,20 @@ void bwd_kernel(BwdParams p) {
 template <typename T, int D, bool MASKED>
 hipError_t launch_bwd_pair(const BwdParams &p, hipStream_t s) {
   using C = BwdCfg<T, D>;
-  hipLaunchKernelGGL((bwd_kernel<T, D, false, MASKED>), dim3(p.B * p.H * p.nqb),
-                     dim3(64 * C::kWavesDq), 0, s, p);
+  if constexpr (C::kRbDqMax >= 2) {
+    if (p.rbq == 2)
+      hipLaunchKernelGGL((bwd_kernel<T, D, false, MASKED, 2>), dim3(p.B * p.H * p.nqb),
+                         dim3(64 * C::kWavesDq), 0, s, p);
+    else
+      hipLaunchKernelGGL((bwd_kernel<T, D, false, MASKED, 1>), dim3(p.B * p.H * p.nqb),
+                         dim3(64 * C::kWavesDq), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((bwd_kernel<T, D, false, MASKED, 1>), dim3(p.B * p.H * p.nqb),
+                       dim3(64 * C::kWavesDq), 0, s, p);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((bwd_kernel<T, D, true, MASKED>), dim3(p.B * p.H * p.nkb),
+  hipLaunchKernelGGL((bwd_kernel<T, D, true, MASKED, 1>), dim3(p.B * p.H * p.nkb),
                      dim3(64 * C::kWavesDkv), 0, s, p);
   return hipGetLastError();
 }

@@ -24,26 +24,30 @@ hipError_t launch_bwd(const BwdParams &p, bool bf16, int d, hipStream_t s) {
   }
 }
 
-bool bwd_shape_for(bool bf16, int d, int *block_q, int *block_k) {
-  auto set = [&](int wq, int wk) {
-    *block_q = 16 * wq;
-    *block_k = 16 * wk;
-    return true;
-  };
+template <typename T, int D>
+bool bwd_rows(int *block_q, int *block_k, int *rbq_max) {
+  using C = BwdCfg<T, D>;
+  *block_q = 16 * C::kWavesDq;
+  *block_k = 16 * C::kWavesDkv;
+  *rbq_max = C::kRbDqMax;
+  return true;
+}
+
+bool bwd_shape_for(bool bf16, int d, int *block_q, int *block_k, int *rbq_max) {
   if (bf16) {
     switch (d) {
-      case 16: return set(BwdCfg<__bf16, 16>::kWavesDq, BwdCfg<__bf16, 16>::kWavesDkv);
-      case 32: return set(BwdCfg<__bf16, 32>::kWavesDq, BwdCfg<__bf16, 32>::kWavesDkv);
-      case 64: return set(BwdCfg<__bf16, 64>::kWavesDq, BwdCfg<__bf16, 64>::kWavesDkv);
-      case 128: return set(BwdCfg<__bf16, 128>::kWavesDq, BwdCfg<__bf16, 128>::kWavesDkv);
-      case 256: return set(BwdCfg<__bf16, 256>::kWavesDq, BwdCfg<__bf16, 256>::kWavesDkv);
+      case 16: return bwd_rows<__bf16, 16>(block_q, block_k, rbq_max);
+      case 32: return bwd_rows<__bf16, 32>(block_q, block_k, rbq_max);
+      case 64: return bwd_rows<__bf16, 64>(block_q, block_k, rbq_max);
+      case 128: return bwd_rows<__bf16, 128>(block_q, block_k, rbq_max);
+      case 256: return bwd_rows<__bf16, 256>(block_q, block_k, rbq_max);
       default: return false;
     }
   }
   switch (d) {
-    case 16: return set(BwdCfg<float, 16>::kWavesDq, BwdCfg<float, 16>::kWavesDkv);
-    case 32: return set(BwdCfg<float, 32>::kWavesDq, BwdCfg<float, 32>::kWavesDkv);
-    case 64: return set(BwdCfg<float, 64>::kWavesDq, BwdCfg<float, 64>::kWavesDkv);
+    case 16: return bwd_rows<float, 16>(block_q, block_k, rbq_max);
+    case 32: return bwd_rows<float, 32>(block_q, block_k, rbq_max);
+    case 64: return bwd_rows<float, 64>(block_q, block_k, rbq_max);
     default: return false;
   }
 }

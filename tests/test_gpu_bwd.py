@@ -189,6 +189,43 @@ def test_backward_frame_window(F, T, C, R, first, last, see_all, dtype, d):
     _say(what, " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
 
 
+def test_backward_two_row_blocks_per_wave():
+    # enough heads that the dQ launch gives each wave two 16-row blocks
+    # (bf16, d = 128, at least 512 workgroups of 256 rows): oracle parity,
+    # and one head equals the same head run alone (one block per wave)
+    w = Workload("bwd2r", 2, 256, 300, 128, "bf16", 9900, tangent_scale=0.1, n_kv=70)
+    _check(w, what="bwd two row blocks")
+    x = make_inputs(w)
+    q, k, v = (x[n].cuda() for n in ("q", "k", "v"))
+    o, _, lse, _ = aj.fwd(*(x[n].cuda() for n in NAMES))
+    go = _grad_input(w, 31).cuda()
+    full = aj.bwd(q, k, v, o, go, lse)
+    b, h = 1, 77
+    one = aj.bwd(*(t[b:b + 1, h:h + 1].contiguous() for t in (q, k, v, o, go, lse)))
+    torch.cuda.synchronize()
+    for a, c in zip(full, one):
+        assert torch.equal(a[b:b + 1, h:h + 1], c)
+
+
+def test_backward_two_row_blocks_frame_window():
+    mask = dict(frames=10, tokens_per_frame=30, chunk_frames=2, radius_chunks=1,
+                anchor_first=1, anchor_last=1, anchor_queries_see_all=0)
+    vis = FrameWindow(frames=10, tokens_per_frame=30, chunk_frames=2, radius_chunks=1)
+    w = Workload("bwd2m", 2, 256, 300, 128, "bf16", 9950, tangent_scale=0.1)
+    x = make_inputs(w)
+    q, k, v = (x[n].cuda() for n in ("q", "k", "v"))
+    o, _, lse, _ = aj.fwd(*(x[n].cuda() for n in NAMES), mask=mask)
+    g_cpu = _grad_input(w, w.seed + 1)
+    gq, gk, gv, _ = aj.bwd(q, k, v, o, g_cpu.cuda(), lse, mask=mask)
+    torch.cuda.synchronize()
+    ref = attention_backward(to_float64(x["q"]), to_float64(x["k"]), to_float64(x["v"]),
+                             to_float64(g_cpu), visible=vis)
+    floor = float(np.max(np.abs(ref[2])))
+    for n, a, r in zip(("dQ", "dK", "dV"), (gq, gk, gv), ref):
+        e = _err(to_float64(a), r, floor)
+        assert e <= TOL["bf16"], f"two row blocks, mask: {n} normwise error {e:.3e}"
+
+
 def test_backward_deterministic():
     w = Workload("bwdd", 1, 2, 500, 128, "bf16", 9400, tangent_scale=0.1, n_kv=700)
     x = make_inputs(w)
