@@ -300,8 +300,8 @@ int check_bwd(const void *Q, const void *K, const void *V, const void *O, const 
     return ATTN_JVP_EINVAL;
   if (dtype != ATTN_JVP_BF16 && dtype != ATTN_JVP_FP32) return ATTN_JVP_EINVAL;
   if (shape->head_dim_v != d) return ATTN_JVP_EUNSUPPORTED;   // the pages: one head dim
-  int bq, bk, rbq_max;
-  if (!attn_jvp::bwd_shape_for(dtype == ATTN_JVP_BF16, d, &bq, &bk, &rbq_max))
+  int bq, bk, rbq_max, rbk_max;
+  if (!attn_jvp::bwd_shape_for(dtype == ATTN_JVP_BF16, d, &bq, &bk, &rbq_max, &rbk_max))
     return ATTN_JVP_EUNSUPPORTED;
   if ((int64_t)B * H * ((Nq + bq - 1) / bq) > 0x7fffffffLL ||
       (int64_t)B * H * ((Nkv + bk - 1) / bk) > 0x7fffffffLL)
@@ -530,14 +530,17 @@ int attn_jvp_bwd(const void *Q, const void *K, const void *V, const void *O, con
   const attn_jvp_bwd_layout L = layout ? *layout : contiguous_bwd(*shape);
   const int st = check_bwd(Q, K, V, O, gO, LSE, gQ, gK, gV, delta, shape, dtype, &L, mask);
   if (st != ATTN_JVP_OK) return st;
-  int bq, bk, rbq_max;
-  attn_jvp::bwd_shape_for(dtype == ATTN_JVP_BF16, shape->head_dim_qk, &bq, &bk, &rbq_max);
-  // two row blocks per dQ wave halve the launch's LDS traffic per MFMA but
-  // also its workgroups: taken while at least two rounds of workgroups
-  // (512 on 256 CUs) remain
-  const int64_t wg2 = (int64_t)shape->batch * shape->heads *
-                      ((shape->seqlen_q + 2 * bq - 1) / (2 * bq));
-  const int rbq = (rbq_max >= 2 && wg2 >= 512) ? 2 : 1;
+  int bq, bk, rbq_max, rbk_max;
+  attn_jvp::bwd_shape_for(dtype == ATTN_JVP_BF16, shape->head_dim_qk, &bq, &bk, &rbq_max,
+                          &rbk_max);
+  // two row blocks per wave halve a launch's LDS traffic per MFMA but also
+  // its workgroups: taken while at least two rounds of workgroups (512 on
+  // 256 CUs) remain
+  const int64_t bh = (int64_t)shape->batch * shape->heads;
+  const int rbq =
+      (rbq_max >= 2 && bh * ((shape->seqlen_q + 2 * bq - 1) / (2 * bq)) >= 512) ? 2 : 1;
+  const int rbk =
+      (rbk_max >= 2 && bh * ((shape->seqlen_kv + 2 * bk - 1) / (2 * bk)) >= 512) ? 2 : 1;
   attn_jvp::BwdParams p;
   memset(&p, 0, sizeof(p));
   p.q = Q; p.k = K; p.v = V; p.o = O; p.g = gO; p.lse = LSE;
@@ -551,8 +554,9 @@ int attn_jvp_bwd(const void *Q, const void *K, const void *V, const void *O, con
   p.Nq = shape->seqlen_q;
   p.Nkv = shape->seqlen_kv;
   p.rbq = rbq;
+  p.rbk = rbk;
   p.nqb = (p.Nq + rbq * bq - 1) / (rbq * bq);
-  p.nkb = (p.Nkv + bk - 1) / bk;
+  p.nkb = (p.Nkv + rbk * bk - 1) / (rbk * bk);
   p.scale = (scale > 0.f && isfinite(scale)) ? scale : 1.0f / sqrtf((float)shape->head_dim_qk);
   p.scale_log2 = p.scale * 1.4426950408889634f;
   p.mask = to_dev(mask);

@@ -47,7 +47,7 @@ struct BwdParams {
   int nqb, nkb;                    // query / key blocks per (b, h)
   float scale, scale_log2;
   MaskDev mask;                    // frame window (kind 0: none); Nq == Nkv when on
-  int rbq;                         // 16-row blocks per dQ wave (1, or 2 where built)
+  int rbq, rbk;                    // 16-row blocks per dQ / dK-dV wave (1, or 2 where built)
 };
 
 // Query-tile ranges [lo, hi) that see some key of rows [k_lo, k_hi) under the
@@ -174,6 +174,9 @@ struct BwdCfg {
   // stays within 128 VGPRs): every streamed LDS fragment then feeds both
   // blocks, halving the LDS bytes per MFMA of the launch that is LDS-bound
   static constexpr int kRbDqMax = (ES == 2 && D == 128) ? 2 : 1;
+  // the same for the key-owned launch where its resident set (K, V
+  // fragments, dK and dV accumulators) stays within 96 VGPRs for two blocks
+  static constexpr int kRbDkvMax = (ES == 2 && D == 64) ? 2 : 1;
   static constexpr int kWavesDkv = kResDkv <= (ES == 2 ? 96 : 48) ? 8 : 4;
   // 64-row tiles while two stages of both tensors fit in 128 KiB and the
   // transposing reads' largest constant offset (stage, second tensor, row
@@ -182,7 +185,7 @@ struct BwdCfg {
   static constexpr int kLds = 4 * kBN * RB;                         // 2 stages x 2 tensors
 };
 
-template <typename T, int D, bool KEYS, bool MASKED, int RBQ>
+template <typename T, int D, bool KEYS, bool MASKED, int RBS>
 __global__ __launch_bounds__((64 * (KEYS ? BwdCfg<T, D>::kWavesDkv : BwdCfg<T, D>::kWavesDq)), 1)
 void bwd_kernel(BwdParams p) {
   using C = BwdCfg<T, D>;
@@ -192,8 +195,8 @@ void bwd_kernel(BwdParams p) {
   using FragV = typename EV::Frag;
   constexpr bool BF16 = sizeof(T) == 2;
   constexpr int W = KEYS ? C::kWavesDkv : C::kWavesDq;
-  constexpr int R = KEYS ? 1 : RBQ;   // 16-row blocks per wave
-  static_assert(R >= 1 && R <= C::kRbDqMax, "row blocks");
+  constexpr int R = RBS;   // 16-row blocks per wave
+  static_assert(R >= 1 && R <= (KEYS ? C::kRbDkvMax : C::kRbDqMax), "row blocks");
   constexpr int BN = C::kBN;
   constexpr int CK = kStepKeys;
   constexpr int NSTEP = BN / CK;
@@ -430,14 +433,16 @@ void bwd_kernel(BwdParams p) {
 
   // accumulators: dQ^T (dQ kernel) or dK^T and dV^T (dK/dV kernel); lane
   // holds d = 16e + 4 lg + 0..3 of its owned row
-  f32x4 acc0[R][ND], acc1[KEYS ? ND : 1];
+  f32x4 acc0[R][ND], acc1[R][KEYS ? ND : 1];
 #pragma unroll
   for (int rb = 0; rb < R; ++rb)
 #pragma unroll
     for (int e = 0; e < ND; ++e) acc0[rb][e] = f32x4{};
   if constexpr (KEYS) {
 #pragma unroll
-    for (int e = 0; e < ND; ++e) acc1[e] = f32x4{};
+    for (int rb = 0; rb < R; ++rb)
+#pragma unroll
+      for (int e = 0; e < ND; ++e) acc1[rb][e] = f32x4{};
   }
 
   const float c2 = p.scale_log2;
@@ -607,7 +612,7 @@ void bwd_kernel(BwdParams p) {
     //                                         shared by the row blocks)
     //  dK/dV kernel: dK^T += Q^T dS, dV^T += G^T P
     if constexpr (BF16) {
-      bf16x8 dsf[R], pf;
+      bf16x8 dsf[R], pf[R];
 #pragma unroll
       for (int rb = 0; rb < R; ++rb)
 #pragma unroll
@@ -615,10 +620,14 @@ void bwd_kernel(BwdParams p) {
           dsf[rb][i] = (__bf16)dsv[rb][0][i];
           dsf[rb][4 + i] = (__bf16)dsv[rb][1][i];
         }
+      if constexpr (KEYS) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pf[i] = (__bf16)pv[0][0][i];
-        pf[4 + i] = (__bf16)pv[0][1][i];
+        for (int rb = 0; rb < R; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            pf[rb][i] = (__bf16)pv[rb][0][i];
+            pf[rb][4 + i] = (__bf16)pv[rb][1][i];
+          }
       }
       constexpr int VO = G * TL + kb * RB;
       constexpr int NR = KEYS ? 4 : 2;          // transposing reads per d block
@@ -650,7 +659,8 @@ void bwd_kernel(BwdParams p) {
         for (int rb = 0; rb < R; ++rb) acc0[rb][e] = EV::mfma(t0f, dsf[rb], acc0[rb][e]);
         if constexpr (KEYS) {
           const FragV t1f = __builtin_bit_cast(FragV, __builtin_shufflevector(cur[2], cur[3], 0, 1, 2, 3, 4, 5, 6, 7));
-          acc1[e] = EV::mfma(t1f, pf, acc1[e]);
+#pragma unroll
+          for (int rb = 0; rb < R; ++rb) acc1[rb][e] = EV::mfma(t1f, pf[rb], acc1[rb][e]);
         }
       });
     } else {
@@ -669,7 +679,9 @@ void bwd_kernel(BwdParams p) {
             for (int rb = 0; rb < R; ++rb) acc0[rb][e] = EV::mfma(t0f, dsv[rb][kb2][i], acc0[rb][e]);
             if constexpr (KEYS) {
               const FragV t1f = *(const FragV *)(Ts + 2 * TL + o);
-              acc1[e] = EV::mfma(t1f, pv[0][kb2][i], acc1[e]);
+#pragma unroll
+              for (int rb = 0; rb < R; ++rb)
+                acc1[rb][e] = EV::mfma(t1f, pv[rb][kb2][i], acc1[rb][e]);
             }
           }
         }
@@ -720,33 +732,38 @@ void bwd_kernel(BwdParams p) {
       for (int e = 0; e < ND; ++e) {
         T4 o;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = (T)acc1[e][i];
+        for (int i = 0; i < 4; ++i) o[i] = (T)acc1[rb][e][i];
         *(T4 *)(O1 + 16 * e + 4 * lg) = o;
       }
     }
   }
 }
 
+// One launch of the dQ (KEYS false) or dK/dV kernel with the row blocks
+// per wave the host chose.
+template <typename T, int D, bool KEYS, bool MASKED>
+hipError_t launch_bwd_one(const BwdParams &p, hipStream_t s) {
+  using C = BwdCfg<T, D>;
+  constexpr int RMAX = KEYS ? C::kRbDkvMax : C::kRbDqMax;
+  const int rb = KEYS ? p.rbk : p.rbq;
+  const dim3 grid(p.B * p.H * (KEYS ? p.nkb : p.nqb));
+  const dim3 block(64 * (KEYS ? C::kWavesDkv : C::kWavesDq));
+  if constexpr (RMAX >= 2) {
+    if (rb == 2) {
+      hipLaunchKernelGGL((bwd_kernel<T, D, KEYS, MASKED, 2>), grid, block, 0, s, p);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((bwd_kernel<T, D, KEYS, MASKED, 1>), grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
 // dQ (and D) first, then dK and dV, on one stream.
 template <typename T, int D, bool MASKED>
 hipError_t launch_bwd_pair(const BwdParams &p, hipStream_t s) {
-  using C = BwdCfg<T, D>;
-  if constexpr (C::kRbDqMax >= 2) {
-    if (p.rbq == 2)
-      hipLaunchKernelGGL((bwd_kernel<T, D, false, MASKED, 2>), dim3(p.B * p.H * p.nqb),
-                         dim3(64 * C::kWavesDq), 0, s, p);
-    else
-      hipLaunchKernelGGL((bwd_kernel<T, D, false, MASKED, 1>), dim3(p.B * p.H * p.nqb),
-                         dim3(64 * C::kWavesDq), 0, s, p);
-  } else {
-    hipLaunchKernelGGL((bwd_kernel<T, D, false, MASKED, 1>), dim3(p.B * p.H * p.nqb),
-                       dim3(64 * C::kWavesDq), 0, s, p);
-  }
-  hipError_t err = hipGetLastError();
+  const hipError_t err = launch_bwd_one<T, D, false, MASKED>(p, s);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((bwd_kernel<T, D, true, MASKED, 1>), dim3(p.B * p.H * p.nkb),
-                     dim3(64 * C::kWavesDkv), 0, s, p);
-  return hipGetLastError();
+  return launch_bwd_one<T, D, true, MASKED>(p, s);
 }
 
 template <typename T, int D>

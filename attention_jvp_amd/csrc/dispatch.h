@@ -38,9 +38,11 @@ hipError_t launch_merge(const MergeParams &m, bool bf16, hipStream_t s);
 // Primal backward (inst_bwd.hip, kernels in bwd.h): d_qk = d_v = d.
 struct BwdParams;
 hipError_t launch_bwd(const BwdParams &p, bool bf16, int d, hipStream_t s);
-// Query rows per dQ workgroup (one 16-row block per wave), key rows per
-// dK/dV workgroup, and the most 16-row blocks a dQ wave may own (the dQ
-// workgroup then covers rbq * block_q rows); false if (dtype, d) is not built.
-bool bwd_shape_for(bool bf16, int d, int *block_q, int *block_k, int *rbq_max);
+// Query rows per dQ workgroup and key rows per dK/dV workgroup with one
+// 16-row block per wave, and the most 16-row blocks a wave of each launch may
+// own (its workgroup then covers that many times the rows); false if
+// (dtype, d) is not built.
+bool bwd_shape_for(bool bf16, int d, int *block_q, int *block_k, int *rbq_max,
+                   int *rbk_max);
 
 }  // namespace attn_jvp

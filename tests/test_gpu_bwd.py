@@ -189,12 +189,14 @@ def test_backward_frame_window(F, T, C, R, first, last, see_all, dtype, d):
     _say(what, " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
 
 
-def test_backward_two_row_blocks_per_wave():
-    # enough heads that the dQ launch gives each wave two 16-row blocks
-    # (bf16, d = 128, at least 512 workgroups of 256 rows): oracle parity,
-    # and one head equals the same head run alone (one block per wave)
-    w = Workload("bwd2r", 2, 256, 300, 128, "bf16", 9900, tangent_scale=0.1, n_kv=70)
-    _check(w, what="bwd two row blocks")
+@pytest.mark.parametrize("d,Nq,Nkv", [(128, 300, 70), (64, 70, 300)])
+def test_backward_two_row_blocks_per_wave(d, Nq, Nkv):
+    # enough heads that a launch gives each wave two 16-row blocks (bf16;
+    # d = 128: the dQ launch, d = 64: the dK/dV launch; at least 512
+    # workgroups of 256 rows): oracle parity, and one head equals the same
+    # head run alone (one block per wave)
+    w = Workload("bwd2r", 2, 256, Nq, d, "bf16", 9900 + d, tangent_scale=0.1, n_kv=Nkv)
+    _check(w, what=f"bwd two row blocks d{d}")
     x = make_inputs(w)
     q, k, v = (x[n].cuda() for n in ("q", "k", "v"))
     o, _, lse, _ = aj.fwd(*(x[n].cuda() for n in NAMES))
@@ -207,11 +209,12 @@ def test_backward_two_row_blocks_per_wave():
         assert torch.equal(a[b:b + 1, h:h + 1], c)
 
 
-def test_backward_two_row_blocks_frame_window():
+@pytest.mark.parametrize("d", [128, 64])
+def test_backward_two_row_blocks_frame_window(d):
     mask = dict(frames=10, tokens_per_frame=30, chunk_frames=2, radius_chunks=1,
                 anchor_first=1, anchor_last=1, anchor_queries_see_all=0)
     vis = FrameWindow(frames=10, tokens_per_frame=30, chunk_frames=2, radius_chunks=1)
-    w = Workload("bwd2m", 2, 256, 300, 128, "bf16", 9950, tangent_scale=0.1)
+    w = Workload("bwd2m", 2, 256, 300, d, "bf16", 9950 + d, tangent_scale=0.1)
     x = make_inputs(w)
     q, k, v = (x[n].cuda() for n in ("q", "k", "v"))
     o, _, lse, _ = aj.fwd(*(x[n].cuda() for n in NAMES), mask=mask)
@@ -223,7 +226,7 @@ def test_backward_two_row_blocks_frame_window():
     floor = float(np.max(np.abs(ref[2])))
     for n, a, r in zip(("dQ", "dK", "dV"), (gq, gk, gv), ref):
         e = _err(to_float64(a), r, floor)
-        assert e <= TOL["bf16"], f"two row blocks, mask: {n} normwise error {e:.3e}"
+        assert e <= TOL["bf16"], f"two row blocks d{d}, mask: {n} normwise error {e:.3e}"
 
 
 def test_backward_deterministic():
