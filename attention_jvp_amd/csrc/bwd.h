@@ -174,10 +174,13 @@ struct BwdCfg {
   // stays within 128 VGPRs): every streamed LDS fragment then feeds both
   // blocks, halving the LDS bytes per MFMA of the launch that is LDS-bound
   static constexpr int kRbDqMax = (ES == 2 && D == 128) ? 2 : 1;
-  // the same for the key-owned launch where its resident set (K, V
-  // fragments, dK and dV accumulators) stays within 96 VGPRs for two blocks
-  static constexpr int kRbDkvMax = (ES == 2 && D == 64) ? 2 : 1;
-  static constexpr int kWavesDkv = kResDkv <= (ES == 2 ? 96 : 48) ? 8 : 4;
+  // the same for the key-owned launch: at d = 64 (96 resident VGPRs for two
+  // blocks, two waves per SIMD) and at d = 128 (192 resident, four waves)
+  static constexpr int kRbDkvMax = (ES == 2 && (D == 64 || D == 128)) ? 2 : 1;
+  // bf16 d = 128 dK/dV: four waves of two 16-row blocks each (the
+  // registers of one wave per SIMD; 5 % faster than eight waves of one)
+  static constexpr int kWavesDkv =
+      (ES == 2 && D == 128) ? 4 : (kResDkv <= (ES == 2 ? 96 : 48) ? 8 : 4);
   // 64-row tiles while two stages of both tensors fit in 128 KiB and the
   // transposing reads' largest constant offset (stage, second tensor, row
   // 48 of the tile) fits the 16-bit DS offset field; else 32
