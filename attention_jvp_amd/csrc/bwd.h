@@ -177,10 +177,12 @@ struct BwdCfg {
   // the same for the key-owned launch: at d = 64 (96 resident VGPRs for two
   // blocks, two waves per SIMD) and at d = 128 (192 resident, four waves)
   static constexpr int kRbDkvMax = (ES == 2 && (D == 64 || D == 128)) ? 2 : 1;
-  // bf16 d = 128 dK/dV: four waves of two 16-row blocks each (the
-  // registers of one wave per SIMD; 5 % faster than eight waves of one)
+  // bf16 d = 128 and d = 64 dK/dV: four waves of two 16-row blocks each
+  // (d = 128: the registers of one wave per SIMD; d = 64: two such
+  // workgroups per CU); 5-9 % faster than eight waves of one block
   static constexpr int kWavesDkv =
-      (ES == 2 && D == 128) ? 4 : (kResDkv <= (ES == 2 ? 96 : 48) ? 8 : 4);
+      (ES == 2 && (D == 128 || D == 64)) ? 4 : (kResDkv <= (ES == 2 ? 96 : 48) ? 8 : 4);
+  static constexpr int kMinBlocksDkv = (ES == 2 && D == 64) ? 2 : 1;
   // 64-row tiles while two stages of both tensors fit in 128 KiB and the
   // transposing reads' largest constant offset (stage, second tensor, row
   // 48 of the tile) fits the 16-bit DS offset field; else 32
@@ -189,7 +191,8 @@ struct BwdCfg {
 };
 
 template <typename T, int D, bool KEYS, bool MASKED, int RBS>
-__global__ __launch_bounds__((64 * (KEYS ? BwdCfg<T, D>::kWavesDkv : BwdCfg<T, D>::kWavesDq)), 1)
+__global__ __launch_bounds__((64 * (KEYS ? BwdCfg<T, D>::kWavesDkv : BwdCfg<T, D>::kWavesDq)),
+                             (KEYS ? BwdCfg<T, D>::kMinBlocksDkv : 1))
 void bwd_kernel(BwdParams p) {
   using C = BwdCfg<T, D>;
   using EK = ElemK<T, D>;
