@@ -169,11 +169,14 @@ struct BwdCfg {
   // dV) accumulator sets
   static constexpr int kResDq = (ES == 2 ? D / 4 : D / 2) + D / 4;
   static constexpr int kResDkv = (ES == 2 ? D / 4 : D / 2) + D / 2;
-  static constexpr int kWavesDq = kResDq <= 96 ? 8 : 4;
-  // bfloat16 d = 128 dQ waves may own two 16-row blocks (the resident set
-  // stays within 128 VGPRs): every streamed LDS fragment then feeds both
-  // blocks, halving the LDS bytes per MFMA of the launch that is LDS-bound
-  static constexpr int kRbDqMax = (ES == 2 && D == 128) ? 2 : 1;
+  // bf16 d = 64 dQ: four waves (of up to two row blocks), two workgroups
+  // per CU (4 % faster at the prefix shape than eight waves)
+  static constexpr int kWavesDq = (ES == 2 && D == 64) ? 4 : (kResDq <= 96 ? 8 : 4);
+  static constexpr int kMinBlocksDq = (ES == 2 && D == 64) ? 2 : 1;
+  // bfloat16 d = 128 and d = 64 dQ waves may own two 16-row blocks (the
+  // resident set stays within 128 VGPRs): every streamed LDS fragment then
+  // feeds both blocks, halving the LDS bytes per MFMA of the LDS-bound launch
+  static constexpr int kRbDqMax = (ES == 2 && (D == 128 || D == 64)) ? 2 : 1;
   // the same for the key-owned launch: at d = 64 (96 resident VGPRs for two
   // blocks, two waves per SIMD) and at d = 128 (192 resident, four waves)
   static constexpr int kRbDkvMax = (ES == 2 && (D == 64 || D == 128)) ? 2 : 1;
@@ -192,7 +195,7 @@ struct BwdCfg {
 
 template <typename T, int D, bool KEYS, bool MASKED, int RBS>
 __global__ __launch_bounds__((64 * (KEYS ? BwdCfg<T, D>::kWavesDkv : BwdCfg<T, D>::kWavesDq)),
-                             (KEYS ? BwdCfg<T, D>::kMinBlocksDkv : 1))
+                             (KEYS ? BwdCfg<T, D>::kMinBlocksDkv : BwdCfg<T, D>::kMinBlocksDq))
 void bwd_kernel(BwdParams p) {
   using C = BwdCfg<T, D>;
   using EK = ElemK<T, D>;
