@@ -21,7 +21,7 @@ __all__ = [
     "attn_jvp_tile_shape_ex", "attn_jvp_visible_tiles", "attn_jvp_fwd_partial",
     "attn_jvp_merge", "attn_jvp_splitkv_plan", "attn_jvp_fwd_splitkv", "exported_symbols",
     "fwd", "fwd_partial", "fwd_splitkv", "merge", "library_path", "load",
-    "BwdLayout", "attn_jvp_bwd", "attn_jvp_bwd_check", "bwd",
+    "BwdLayout", "attn_jvp_bwd", "attn_jvp_bwd_check", "attn_jvp_bwd_visible_tiles", "bwd",
 ]
 
 ATTN_JVP_BF16 = 0
@@ -70,7 +70,7 @@ EXPORTS = ("attn_jvp_fwd", "attn_jvp_fwd_strided", "attn_jvp_fwd_ex", "attn_jvp_
            "attn_jvp_check_ex", "attn_jvp_tile_shape", "attn_jvp_tile_shape_ex",
            "attn_jvp_visible_tiles", "attn_jvp_fwd_partial", "attn_jvp_merge",
            "attn_jvp_splitkv_plan", "attn_jvp_fwd_splitkv", "attn_jvp_bwd",
-           "attn_jvp_bwd_check", "attn_jvp_status_string")
+           "attn_jvp_bwd_check", "attn_jvp_bwd_visible_tiles", "attn_jvp_status_string")
 
 
 def library_path():
@@ -128,6 +128,8 @@ def load():
     lib.attn_jvp_tile_shape.restype = i32
     lib.attn_jvp_visible_tiles.argtypes = [i32, i32, i32, ctypes.POINTER(Mask), i64p]
     lib.attn_jvp_visible_tiles.restype = i32
+    lib.attn_jvp_bwd_visible_tiles.argtypes = [i32, i32, i32, i32, ctypes.POINTER(Mask), i64p]
+    lib.attn_jvp_bwd_visible_tiles.restype = i32
     lib.attn_jvp_status_string.argtypes = [i32]
     lib.attn_jvp_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -252,6 +254,15 @@ def attn_jvp_visible_tiles(N, dtype, d, mask=None):
     st = load().attn_jvp_visible_tiles(N, dtype, d, _mask_ptr(mask), out)
     if st != 0:
         raise AttnJvpError(st, "attn_jvp_visible_tiles")
+    return list(out)
+
+
+def attn_jvp_bwd_visible_tiles(N, block_rows, tile_rows, keys, mask=None):
+    out = (ctypes.c_int64 * ((N + block_rows - 1) // block_rows))()
+    st = load().attn_jvp_bwd_visible_tiles(N, block_rows, tile_rows, int(bool(keys)),
+                                           _mask_ptr(mask), out)
+    if st != 0:
+        raise AttnJvpError(st, "attn_jvp_bwd_visible_tiles")
     return list(out)
 
 

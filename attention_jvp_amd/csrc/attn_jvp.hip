@@ -630,6 +630,25 @@ int attn_jvp_visible_tiles(int N, int dtype, int d, const attn_jvp_mask *mask,
   return ATTN_JVP_OK;
 }
 
+int attn_jvp_bwd_visible_tiles(int N, int block_rows, int tile_rows, int keys,
+                               const attn_jvp_mask *mask, int64_t *tiles_per_block) {
+  if (N <= 0 || block_rows <= 0 || tile_rows <= 0 || !tiles_per_block) return ATTN_JVP_EINVAL;
+  const int mst = check_mask(mask, N, N);
+  if (mst != ATTN_JVP_OK) return mst;
+  const MaskDev m = to_dev(mask);
+  const int nb = (N + block_rows - 1) / block_rows;
+  for (int b = 0; b < nb; ++b) {
+    const int r0 = b * block_rows;
+    const int r1 = r0 + block_rows < N ? r0 + block_rows : N;
+    const attn_jvp::TileRanges tr = keys ? attn_jvp::visible_query_tiles(m, r0, r1, N, tile_rows)
+                                         : attn_jvp::visible_tiles(m, r0, r1, N, tile_rows);
+    int64_t c = 0;
+    for (int i = 0; i < tr.n; ++i) c += tr.hi[i] - tr.lo[i];
+    tiles_per_block[b] = c;
+  }
+  return ATTN_JVP_OK;
+}
+
 const char *attn_jvp_status_string(int status) {
   switch (status) {
     case ATTN_JVP_OK: return "ok";

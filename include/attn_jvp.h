@@ -283,6 +283,18 @@ int attn_jvp_tile_shape_ex(int dtype, int d_qk, int d_v, int *block_m, int *bloc
 int attn_jvp_visible_tiles(int N, int dtype, int d, const attn_jvp_mask *mask,
                            int64_t *tiles_per_block);
 
+/* Host-only: the streamed tiles the two backward launches walk under `mask`
+ * (NULL = dense) for an N-token sequence whose owned rows are cut into blocks
+ * of block_rows and whose streamed rows are cut into tiles of tile_rows:
+ * keys == 0 gives, per query block, the key tiles of the dQ launch; keys != 0
+ * gives, per key block, the query tiles of the dK/dV launch (a block holding
+ * an anchor key is seen by every query).  Writes ceil(N / block_rows) counts
+ * into tiles_per_block (host memory, caller-owned); returns a status.  With
+ * the block and tile rows a launch uses, this is the exact work list it
+ * walks. */
+int attn_jvp_bwd_visible_tiles(int N, int block_rows, int tile_rows, int keys,
+                               const attn_jvp_mask *mask, int64_t *tiles_per_block);
+
 /* Static English text for a status code. */
 const char *attn_jvp_status_string(int status);
 

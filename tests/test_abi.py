@@ -221,6 +221,40 @@ def test_scheduler_visits_exactly_the_visible_tiles(F, T, C, R, first, last, see
     assert got == _tiles_with_visible_pairs(w, N, bm, bn)
 
 
+def _bwd_tiles_with_visible_pairs(w, N, block, tile, keys):
+    # brute force: per owned block, the streamed tiles holding a pair the
+    # oracle's window shows (owned rows are keys when `keys`)
+    idx = np.arange(N)
+    out = []
+    for r0 in range(0, N, block):
+        rows = np.arange(r0, min(r0 + block, N))
+        vis = (w(idx, rows) if keys else w(rows, idx)).any(axis=1 if keys else 0)
+        out.append(len({j // tile for j in np.nonzero(vis)[0]}))
+    return out
+
+
+@pytest.mark.parametrize("F,T,C,R,first,last,see_all", [
+    (21, 100, 3, 1, 1, 0, 0),
+    (17, 37, 2, 0, 0, 1, 0),
+    (9, 300, 4, 2, 0, 0, 0),
+    (50, 7, 1, 0, 1, 1, 1),
+    (12, 64, 2, 0, 1, 1, 1),
+    (14, 90, 3, 1, 0, 0, 1),
+])
+@pytest.mark.parametrize("block,tile", [(64, 64), (128, 64), (256, 32)])
+def test_backward_scheduler_visits_exactly_the_visible_tiles(F, T, C, R, first, last, see_all,
+                                                             block, tile):
+    N = F * T
+    mask = dict(frames=F, tokens_per_frame=T, chunk_frames=C, radius_chunks=R,
+                anchor_first=first, anchor_last=last, anchor_queries_see_all=see_all)
+    w = FrameWindow(F, T, C, R, bool(first), bool(last), bool(see_all))
+    for keys in (0, 1):
+        got = aj.attn_jvp_bwd_visible_tiles(N, block, tile, keys, mask)
+        assert got == _bwd_tiles_with_visible_pairs(w, N, block, tile, keys), (keys, got)
+    dense = aj.attn_jvp_bwd_visible_tiles(N, block, tile, 1)
+    assert dense == [(N + tile - 1) // tile] * ((N + block - 1) // block)
+
+
 def test_dense_scheduler_visits_every_tile():
     got = aj.attn_jvp_visible_tiles(4352, 0, 64)
     assert got == [68] * 34
