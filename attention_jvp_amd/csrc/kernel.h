@@ -501,6 +501,12 @@ __global__ __launch_bounds__((Cfg<T, DQK, DV>::kThreads), 1) void attn_jvp_kerne
     kcopy.issue(k0, Nkv, smem + g * TK, 2 * TK);
     vcopy.issue(k0, Nkv, smem + VB + g * TV, 2 * TV);
   };
+  auto issue_k = [&](int it, int g) __attribute__((always_inline)) {
+    kcopy.issue(tile_at(tr, t_first + it) * BN, Nkv, smem + g * TK, 2 * TK);
+  };
+  auto issue_v = [&](int it, int g) __attribute__((always_inline)) {
+    vcopy.issue(tile_at(tr, t_first + it) * BN, Nkv, smem + VB + g * TV, 2 * TV);
+  };
   if (ntile > 0) issue_tile(0, 0);
 
   const int qrow = q0 + wave * kWaveRows + qi;
@@ -802,9 +808,16 @@ __global__ __launch_bounds__((Cfg<T, DQK, DV>::kThreads), 1) void attn_jvp_kerne
     const bool need = needs_mask(k0);
     wait_vmem();
     __syncthreads();   // tile `it` landed; every wave is done with tile it-1
-    if (it + 1 < ntile) issue_tile(it + 1, 1 - decltype(G_)::value);
     f32x4 sa[2], dsa[2];
     scores(G_, C0{}, sa, dsa);
+    // the next tile's copies go out behind MFMA work (K and dK after the
+    // first scores, V and dV after the second step's scores where the order
+    // overlaps), not at the barrier where every wave would issue them while
+    // the matrix cores idle
+    if (it + 1 < ntile) issue_k(it + 1, 1 - decltype(G_)::value);
+    if constexpr (!kOverlap) {
+      if (it + 1 < ntile) issue_v(it + 1, 1 - decltype(G_)::value);
+    }
     if (need) apply_mask(k0, sa, dsa);
     update_max(sa);
     if constexpr (NSTEP == 1) {
@@ -818,6 +831,7 @@ __global__ __launch_bounds__((Cfg<T, DQK, DV>::kThreads), 1) void attn_jvp_kerne
         // the exponentials of a are computed here, beside the scores of b,
         // not sunk past the mask branch below
         asm volatile("" ::"v"(sa[0]), "v"(sa[1]), "v"(dsa[0]), "v"(dsa[1]));
+        if (it + 1 < ntile) issue_v(it + 1, 1 - decltype(G_)::value);
         if (need) apply_mask(k0 + CK, sb, dsb);
         accumulate(G_, C0{}, sa, dsa);
       } else {
