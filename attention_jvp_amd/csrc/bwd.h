@@ -485,8 +485,9 @@ void bwd_kernel(BwdParams p) {
   // rows: LDS address of the tile's query-term slot (dK/dV kernel); tail:
   // the tile holds streamed rows past the end (dQ kernel masks those keys);
   // need: the tile is partly visible under the frame window
-  auto step = [&](auto G_, auto KC_, int t0, uint32_t rows, bool tail, bool need)
-                  __attribute__((always_inline)) {
+  // after_scores runs once the step's score MFMAs are issued
+  auto step = [&](auto G_, auto KC_, int t0, uint32_t rows, bool tail, bool need,
+                  auto &&after_scores) __attribute__((always_inline)) {
     constexpr int G = decltype(G_)::value;
     constexpr int kb = decltype(KC_)::value * CK;
     f32x4 nl2[2], y0[2];
@@ -571,6 +572,7 @@ void bwd_kernel(BwdParams p) {
         }
       }
     }
+    after_scores();
     // P and dS = P (.) (dP - D), unscaled
     f32x4 pv[R][2], dsv[R][2];
 #pragma unroll
@@ -700,17 +702,23 @@ void bwd_kernel(BwdParams p) {
   auto tile = [&](auto G_, int it) __attribute__((always_inline)) {
     wait_vmem();
     __syncthreads();   // tile `it` landed; every wave is done with tile it-1
-    if (it + 1 < ntile) issue_tile(it + 1, 1 - decltype(G_)::value);
-    if constexpr (KEYS) {
-      if (it + 2 < ntile) issue_rows(it + 2);
-      if (it + 1 < ntile) transform_rows(it + 1);
-    }
     const uint32_t rows = rows_a + (it % 3) * kRowSlot;
     const int t0 = tile_at(tr, it) * BN;
     const bool tail = t0 + BN > Nstr;
     const bool need = needs_mask(t0);
+    // the next tile's copies (and the query-term rows) go out behind the
+    // first step's score MFMAs, not at the barrier
+    auto next = [&]() __attribute__((always_inline)) {
+      if (it + 1 < ntile) issue_tile(it + 1, 1 - decltype(G_)::value);
+      if constexpr (KEYS) {
+        if (it + 2 < ntile) issue_rows(it + 2);
+        if (it + 1 < ntile) transform_rows(it + 1);
+      }
+    };
+    auto none = []() __attribute__((always_inline)) {};
     static_for<0, NSTEP>([&](auto kc) __attribute__((always_inline)) {
-      step(G_, kc, t0, rows, tail, need);
+      if constexpr (decltype(kc)::value == 0) step(G_, kc, t0, rows, tail, need, next);
+      else step(G_, kc, t0, rows, tail, need, none);
     });
   };
 
