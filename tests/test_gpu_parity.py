@@ -140,6 +140,46 @@ def test_strided_bshd_views():
     _compare([to_float64(t) for t in out], ref, "bf16", "bshd")
 
 
+def _far_batch_view(t, sb):
+    # a [B, H, N, d] view whose batch stride sb is beyond 2^31 elements:
+    # 64-bit element offsets in every address of the path
+    B, H, N, d = t.shape
+    base = torch.empty(sb * (B - 1) + H * N * d, device="cuda", dtype=t.dtype)
+    v = base.as_strided((B, H, N, d), (sb, N * d, d, 1))
+    v.copy_(t.cuda())
+    return v
+
+
+def test_batch_stride_beyond_2_31_elements():
+    sb = (1 << 31) + (1 << 20)
+    w = Workload("far", 2, 1, 256, 128, "bf16", 14, tangent_scale=0.1)
+    x = make_inputs(w)
+    g = {n: _far_batch_view(x[n], sb) for n in NAMES}
+    o = _far_batch_view(torch.zeros_like(x["q"]), sb)
+    do = _far_batch_view(torch.zeros_like(x["q"]), sb)
+    lse = torch.empty((2, 1, 256), device="cuda")
+    dlse = torch.empty_like(lse)
+    aj.fwd(*(g[n] for n in NAMES), out=(o, do, lse, dlse))
+    torch.cuda.synchronize()
+    ref = attention_jvp(*(to_float64(x[n]) for n in NAMES))
+    _compare([to_float64(t) for t in (o, do, lse, dlse)], ref, "bf16", "far batch stride")
+    # the primal backward on the same far views
+    from oracle import attention_backward
+    gcpu = torch.from_numpy(np.random.default_rng(15).standard_normal((2, 1, 256, 128))).bfloat16()
+    go = _far_batch_view(gcpu, sb)
+    outs = (_far_batch_view(torch.zeros_like(x["q"]), sb), _far_batch_view(torch.zeros_like(x["k"]), sb),
+            _far_batch_view(torch.zeros_like(x["v"]), sb), torch.empty((2, 1, 256), device="cuda"))
+    gq, gk, gv, _ = aj.bwd(g["q"], g["k"], g["v"], o, go, lse, out=outs)
+    torch.cuda.synchronize()
+    refb = attention_backward(to_float64(x["q"]), to_float64(x["k"]), to_float64(x["v"]),
+                              to_float64(gcpu))
+    for n, a, r in zip(("dQ", "dK", "dV"), (gq, gk, gv), refb):
+        err = float(np.max(np.abs(to_float64(a) - r)) / np.max(np.abs(r)))
+        assert err <= 2e-2, f"far batch stride backward: {n} normwise error {err:.3e}"
+    del g, o, do, go, outs
+    torch.cuda.empty_cache()
+
+
 def test_contiguous_entry_point_raw_pointers():
     w = Workload("raw", 1, 2, 200, 64, "bf16", 12, tangent_scale=0.1)
     x = make_inputs(w)
