@@ -96,8 +96,8 @@ __host__ __device__ inline TileRanges visible_query_tiles(const MaskDev &m, int 
 
 // Global->LDS copies of the streamed tiles: SideCopier's scheme (1 KiB per
 // wave instruction, lane-chosen swizzled chunk, clamped tail rows) for two
-// tensors with their own row strides.
-template <typename T, int RB, int BN, int W>
+// tensors with their own row strides; KS is the swizzle kind of lds_off.
+template <typename T, int RB, int BN, int W, int KS>
 struct PairCopier {
   static constexpr int CPR = RB / 16;
   static constexpr int TILE = BN * RB;
@@ -123,7 +123,7 @@ struct PairCopier {
     for (int i = 0; i < IPW; ++i) {
       const int s = (i * W + wave) * 64 + lane;
       const int r = s / CPR;
-      const int c = (s % CPR) ^ kswz<RB>(r);
+      const int c = (s % CPR) ^ swz<RB, KS>(r);
       slot[i] = ((uint32_t)r << 16) | (uint32_t)c;
     }
   }
@@ -216,6 +216,11 @@ void bwd_kernel(BwdParams p) {
   constexpr int ND = D / 16;
   constexpr float kLog2e = 1.4426950408889634f;
   constexpr int kRowSlot = 3 * 256;    // bytes of one slot of query-term rows
+  // The streamed tiles are read both along rows (score operands) and
+  // transposed (product operands): bfloat16 tiles take the swizzle that is
+  // conflict-free for both; the float32 products read single elements,
+  // where the operand-row rule does best.
+  constexpr int KSW = BF16 ? kSwzB : kSwzK;
 
   // tiles, then (dK/dV kernel) three slots x 3 rows of 64 floats of query
   // terms: row 0 -LSE log2 e, row 1 -D, row 2 a landing row for the waves
@@ -346,7 +351,7 @@ void bwd_kernel(BwdParams p) {
   // streamed tiles: both tensors have rows of D elements, one copier; the
   // same tile is read as operand rows and through transposing loads, so
   // one swizzle (the operand-row rule) serves both
-  PairCopier<T, RB, BN, W> copier;
+  PairCopier<T, RB, BN, W, KSW> copier;
   copier.init(S0, S1, ss0, ss1, wave, lane);
   // dK/dV kernel: the streamed query rows' LSE and D come as 4-byte
   // global->LDS copies (64 rows per wave instruction) into slot it % 3, two
@@ -459,12 +464,12 @@ void bwd_kernel(BwdParams p) {
   uint32_t rdl[DS];                          // operand-row reads, k-step s
 #pragma unroll
   for (int s = 0; s < DS; ++s)
-    rdl[s] = smem_a + lds_off<RB, true>(rl, (s * KI + lg * KL) * (int)sizeof(T));
+    rdl[s] = smem_a + lds_off<RB, KSW>(rl, (s * KI + lg * KL) * (int)sizeof(T));
   uint32_t trl[BF16 ? ND : 1];               // transposing reads, d block e
   if constexpr (BF16) {
 #pragma unroll
     for (int e = 0; e < ND; ++e)
-      trl[e] = smem_a + lds_off<RB, true>(4 * lg + (rl >> 2), (16 * e + 4 * (rl & 3)) * 2);
+      trl[e] = smem_a + lds_off<RB, KSW>(4 * lg + (rl >> 2), (16 * e + 4 * (rl & 3)) * 2);
   }
 
   // dQ kernel: -LSE log2 e of the lane's query (-inf for a row with no
@@ -684,7 +689,7 @@ void bwd_kernel(BwdParams p) {
           const int r = kb + 16 * kb2 + 4 * lg + i;
 #pragma unroll
           for (int e = 0; e < ND; ++e) {
-            const int o = lds_off<RB, true>(r, (16 * e + rl) * 4);
+            const int o = lds_off<RB, KSW>(r, (16 * e + rl) * 4);
             const FragV t0f = *(const FragV *)(Ts + o);
 #pragma unroll
             for (int rb = 0; rb < R; ++rb) acc0[rb][e] = EV::mfma(t0f, dsv[rb][kb2][i], acc0[rb][e]);
