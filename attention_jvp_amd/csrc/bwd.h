@@ -138,11 +138,15 @@ struct PairCopier {
       uint32_t r = slot[i] >> 16;
       r = r < (uint32_t)valid ? r : (uint32_t)valid;
       const uint32_t c16 = (slot[i] & 0xffffu) << 4;
+      // 32-bit lane offsets from a wave-uniform base: the copies take the
+      // scalar-base address form (no 64-bit address arithmetic per lane);
+      // r < BN and the strides are below 2^24 bytes, so they fit
+      const uint32_t off0 = __umul24(r, rs[0]) + c16;
+      const uint32_t off1 = __umul24(r, rs[1]) + c16;
       char *dst = dst0 + (i * W + wave) * 1024;
-      __builtin_amdgcn_global_load_lds((const void *)(tb0 + __umul24(r, rs[0]) + c16),
-                                       (lds_void *)dst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void *)(tb1 + __umul24(r, rs[1]) + c16),
-                                       (lds_void *)(dst + tstride), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(tb0 + off0), (lds_void *)dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(tb1 + off1), (lds_void *)(dst + tstride),
+                                       16, 0, 0);
     }
   }
 };
