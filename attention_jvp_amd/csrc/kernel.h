@@ -73,8 +73,14 @@ struct Cfg {
   // VGPRs per lane that stay resident: Q and dQ fragments, O, A, B blocks.
   // Two waves per SIMD (256 VGPRs each) while they leave room for the step's
   // working set; float32 score steps need more of it (one k-step per 4 d).
+  // bfloat16 d_qk = d_v = 64 (152 VGPRs) runs three waves per SIMD: its
+  // softmax VALU work per MFMA is twice that of d = 128, and a third wave
+  // per SIMD keeps the matrix cores fed (measured 7-12 % faster per
+  // workgroup; at d = 16 and 32 a third wave was slower).
   static constexpr int kResident = (ES == 2 ? DQK / 4 : DQK / 2) + 3 * DV / 4;
-  static constexpr int kWaves = kResident <= (ES == 2 ? 128 : 64) ? 8 : 4;
+  static constexpr int kWaves = (ES == 2 && DQK == 64 && DV == 64)
+                                    ? 12
+                                    : (kResident <= (ES == 2 ? 128 : 64) ? 8 : 4);
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kBlockM = kWaveRows * kWaves;
   static constexpr int kBN = 4 * 64 * (RBK + RBV) <= 128 * 1024 ? 64 : 32;

@@ -127,7 +127,7 @@ def test_status_strings():
 
 def test_tile_shape():
     assert aj.attn_jvp_tile_shape(0, 128) == (128, 64)
-    assert aj.attn_jvp_tile_shape(0, 64) == (128, 64)
+    assert aj.attn_jvp_tile_shape(0, 64) == (192, 64)     # bf16 d = 64: twelve waves
     assert aj.attn_jvp_tile_shape(1, 64) == (64, 64)     # float32: four waves
     with pytest.raises(aj.AttnJvpError):
         aj.attn_jvp_tile_shape(1, 128)
@@ -257,7 +257,7 @@ def test_backward_scheduler_visits_exactly_the_visible_tiles(F, T, C, R, first, 
 
 def test_dense_scheduler_visits_every_tile():
     got = aj.attn_jvp_visible_tiles(4352, 0, 64)
-    assert got == [68] * 34
+    assert got == [68] * 23          # 192-row query blocks at bf16 d = 64
 
 
 def test_long_video_visited_fraction():
