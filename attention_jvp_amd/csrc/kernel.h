@@ -833,6 +833,16 @@ __global__ __launch_bounds__((Cfg<T, DQK, DV>::kThreads), 1) void attn_jvp_kerne
   // behind a branch that is uniform over the tile, placed where the order
   // already ends a block.
   constexpr bool kOverlap = BF16 && NSTEP == 2 && DQK + DV >= 256;
+  // In the overlapped schedule a wave issues its MFMA blocks at raised
+  // priority: where both waves of a SIMD have an instruction ready, the one
+  // feeding the matrix core goes first and the other's VALU and LDS work
+  // fills the MFMAs' shadow (3-5 % at d = 128; at d = 64 and 32, with three
+  // and two waves per SIMD and the plain order, it did not help).
+  auto mfma_block = [&](auto &&body) __attribute__((always_inline)) {
+    if constexpr (kOverlap) __builtin_amdgcn_s_setprio(1);
+    body();
+    if constexpr (kOverlap) __builtin_amdgcn_s_setprio(0);
+  };
   auto tile = [&](auto G_, int it) __attribute__((always_inline)) {
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
@@ -841,7 +851,7 @@ __global__ __launch_bounds__((Cfg<T, DQK, DV>::kThreads), 1) void attn_jvp_kerne
     wait_vmem();
     __syncthreads();   // tile `it` landed; every wave is done with tile it-1
     f32x4 sa[2], dsa[2];
-    scores(G_, C0{}, sa, dsa);
+    mfma_block([&]() __attribute__((always_inline)) { scores(G_, C0{}, sa, dsa); });
     // the next tile's copies go out behind MFMA work (K and dK after the
     // first scores, V and dV after the second step's scores where the order
     // overlaps), not at the barrier where every wave would issue them while
@@ -854,27 +864,27 @@ __global__ __launch_bounds__((Cfg<T, DQK, DV>::kThreads), 1) void attn_jvp_kerne
     update_max(sa);
     if constexpr (NSTEP == 1) {
       softmax(sa, dsa);
-      accumulate(G_, C0{}, sa, dsa);
+      mfma_block([&]() __attribute__((always_inline)) { accumulate(G_, C0{}, sa, dsa); });
     } else {
       f32x4 sb[2], dsb[2];
       if constexpr (kOverlap) {
-        scores(G_, C1{}, sb, dsb);
+        mfma_block([&]() __attribute__((always_inline)) { scores(G_, C1{}, sb, dsb); });
         softmax(sa, dsa);
         // the exponentials of a are computed here, beside the scores of b,
         // not sunk past the mask branch below
         asm volatile("" ::"v"(sa[0]), "v"(sa[1]), "v"(dsa[0]), "v"(dsa[1]));
         if (it + 1 < ntile) issue_v(it + 1, 1 - decltype(G_)::value);
         if (need) apply_mask(k0 + CK, sb, dsb);
-        accumulate(G_, C0{}, sa, dsa);
+        mfma_block([&]() __attribute__((always_inline)) { accumulate(G_, C0{}, sa, dsa); });
       } else {
         softmax(sa, dsa);
-        accumulate(G_, C0{}, sa, dsa);
-        scores(G_, C1{}, sb, dsb);
+        mfma_block([&]() __attribute__((always_inline)) { accumulate(G_, C0{}, sa, dsa); });
+        mfma_block([&]() __attribute__((always_inline)) { scores(G_, C1{}, sb, dsb); });
         if (need) apply_mask(k0 + CK, sb, dsb);
       }
       update_max(sb);
       softmax(sb, dsb);
-      accumulate(G_, C1{}, sb, dsb);
+      mfma_block([&]() __attribute__((always_inline)) { accumulate(G_, C1{}, sb, dsb); });
     }
   };
 
