@@ -21,8 +21,9 @@
 //   * K, dK, V, dV tiles move global -> LDS with asynchronous
 //     global_load_lds_dwordx4 copies into two LDS stages (the next tile
 //     streams in while the current one is consumed; no register staging),
-//     row-major with an XOR swizzle of the 16-byte chunks (one rule for the
-//     operand-row reads of K and dK, one for the transposing reads of V, dV);
+//     row-major with an XOR swizzle of the 16-byte chunks chosen from the
+//     measured LDS bank geometry (K and dK for operand-row reads, V and dV
+//     for transposing reads; both conflict-free);
 //   * the score products read their K and dK slices two or three slices
 //     ahead of the MFMAs that use them, with explicit LDS waits;
 //   * the value products need V and dV transposed (keys along the MFMA k
@@ -36,9 +37,13 @@
 //     on the same XCD (dispatch round-robins consecutive ids over the 8 XCDs),
 //     keeping that head's K/V/dK/dV in one L2;
 //   * with a frame-window mask, each query block walks only the key-tile
-//     ranges some of its rows can see; element masks run on partial tiles.
+//     ranges some of its rows can see; element masks run on partial tiles;
+//   * at d_qk + d_v >= 256 a step's MFMA blocks run at raised wave priority,
+//     so that of the two waves of a SIMD the one feeding the matrix core
+//     issues first.
 // Eight waves (two per SIMD) when the resident registers allow it, else four;
-// 64-key tiles when two stages fit in 128 KiB of LDS, else 32-key tiles.
+// twelve (three per SIMD) at bf16 d_qk = d_v = 64; 64-key tiles when two
+// stages fit in 128 KiB of LDS, else 32-key tiles.
 // float32 inputs use the same structure with v_mfma_f32_16x16x4_f32.
 
 #pragma once
