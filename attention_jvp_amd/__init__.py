@@ -70,7 +70,8 @@ EXPORTS = ("attn_jvp_fwd", "attn_jvp_fwd_strided", "attn_jvp_fwd_ex", "attn_jvp_
            "attn_jvp_check_ex", "attn_jvp_tile_shape", "attn_jvp_tile_shape_ex",
            "attn_jvp_visible_tiles", "attn_jvp_fwd_partial", "attn_jvp_merge",
            "attn_jvp_splitkv_plan", "attn_jvp_fwd_splitkv", "attn_jvp_bwd",
-           "attn_jvp_bwd_check", "attn_jvp_bwd_visible_tiles", "attn_jvp_status_string")
+           "attn_jvp_bwd_check", "attn_jvp_bwd_visible_tiles", "attn_jvp_status_string",
+           "attn_jvp_build_id")
 
 
 def library_path():
@@ -86,6 +87,14 @@ def load():
     if not os.path.exists(path):
         raise ImportError(f"{path} is not built; run `python -m attention_jvp_amd.build`")
     lib = ctypes.CDLL(path)
+    # refuse a library built from other sources than the ones beside it
+    from .build import source_digest
+    lib.attn_jvp_build_id.argtypes = []
+    lib.attn_jvp_build_id.restype = ctypes.c_char_p
+    built, now = lib.attn_jvp_build_id().decode(), source_digest()
+    if built != now:
+        raise ImportError(f"{path} was built from other sources (build id {built[:12]}, "
+                          f"sources {now[:12]}); rebuild with `python -m attention_jvp_amd.build`")
     vp, i32, f32, i64p = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.POINTER(ctypes.c_int64)
     ptrs10 = [vp] * 6 + [vp, vp, vp, vp]
     lib.attn_jvp_fwd.argtypes = ptrs10 + [i32, i32, i32, i32, f32, i32, ctypes.POINTER(Mask), vp]
@@ -271,6 +280,16 @@ def attn_jvp_status_string(status):
 
 
 # ---- torch convenience ----------------------------------------------------
+#
+# Every tensor the caller hands over (inputs, ``out=`` tensors, the saved lse,
+# a workspace) is checked here for shape, dtype, device and, where the C side
+# assumes it, contiguity, before any pointer reaches the library: the C entry
+# points see raw addresses only and cannot detect a short or misplaced buffer.
+
+def _torch_dtypes():
+    import torch
+    return {torch.bfloat16: ATTN_JVP_BF16, torch.float32: ATTN_JVP_FP32}
+
 
 def _strides3(t):
     s = t.stride()
@@ -287,54 +306,31 @@ def layout_of(q, k, v, dq, dk, dv, o, do):
     return lay
 
 
-def fwd(q, k, v, dq, dk, dv, scale=None, mask=None, out=None):
-    """(o, do, lse, dlse) for CUDA tensors q [B, H, Lq, d_qk], k [B, H, Lkv,
-    d_qk], v [B, H, Lkv, d_v] (bf16 or float32).
+def _require_gpu(t, what):
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be on a GPU device, got {t.device}")
 
-    Tangents must have their primal's shape and strides.  ``mask`` is None or
-    a frame-window dict/Mask (self-attention, Lq == Lkv).  Outputs o, do
-    [B, H, Lq, d_v] and lse, dlse [B, H, Lq] are allocated contiguous unless
-    ``out = (o, do, lse, dlse)`` is given.  Runs on the current stream.
-    """
+
+def check_tensor(t, name, shape, dtype, device, contiguous=False):
+    """Raise ValueError unless ``t`` is a tensor of this shape, dtype and
+    device (and contiguous when asked)."""
     import torch
-    dtypes = {torch.bfloat16: ATTN_JVP_BF16, torch.float32: ATTN_JVP_FP32}
-    if q.dtype not in dtypes:
-        raise TypeError(f"unsupported dtype {q.dtype}")
-    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
-        raise ValueError("q, k, v must be 4-d [B, H, L, d]")
-    B, H, Lq, dqk = q.shape
-    Lkv, dv_ = k.shape[2], v.shape[3]
-    if tuple(k.shape) != (B, H, Lkv, dqk) or tuple(v.shape) != (B, H, Lkv, dv_):
-        raise ValueError("shapes must be q [B,H,Lq,d_qk], k [B,H,Lkv,d_qk], v [B,H,Lkv,d_v]")
-    for t, ref in ((dq, q), (dk, k), (dv, v)):
-        if t.shape != ref.shape:
-            raise ValueError("each tangent must have its primal's shape")
-    for t in (k, v, dq, dk, dv):
-        if t.dtype != q.dtype or t.device != q.device:
-            raise ValueError("q, k, v, dq, dk, dv must share dtype and device")
-    if out is None:
-        o = torch.empty((B, H, Lq, dv_), device=q.device, dtype=q.dtype)
-        do = torch.empty_like(o)
-        lse = torch.empty((B, H, Lq), device=q.device, dtype=torch.float32)
-        dlse = torch.empty_like(lse)
-    else:
-        o, do, lse, dlse = out
-    lay = layout_of(q, k, v, dq, dk, dv, o, do)
-    shape = Shape(B, H, Lq, Lkv, dqk, dv_)
-    stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = attn_jvp_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), dq.data_ptr(),
-                         dk.data_ptr(), dv.data_ptr(), o.data_ptr(), do.data_ptr(),
-                         lse.data_ptr(), dlse.data_ptr(), shape,
-                         0.0 if scale is None else float(scale), dtypes[q.dtype],
-                         lay, mask, stream)
-    if st != 0:
-        raise AttnJvpError(st, "attn_jvp_fwd_ex")
-    return o, do, lse, dlse
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor, got {type(t).__name__}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
 
 
-def _check_qkv(q, k, v, dq, dk, dv):
-    import torch
-    dtypes = {torch.bfloat16: ATTN_JVP_BF16, torch.float32: ATTN_JVP_FP32}
+def check_qkv(q, k, v, dq, dk, dv):
+    """(dtype code, Shape) of a JVP call's inputs; raises on any mismatch of
+    shape, dtype or device between them."""
+    dtypes = _torch_dtypes()
     if q.dtype not in dtypes:
         raise TypeError(f"unsupported dtype {q.dtype}")
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
@@ -352,16 +348,66 @@ def _check_qkv(q, k, v, dq, dk, dv):
     return dtypes[q.dtype], Shape(B, H, Lq, Lkv, dqk, dv_)
 
 
+def check_fwd_out(out, q, shape, out_dtype=None):
+    """Validate ``out = (o, do, lse, dlse)`` of a JVP call: o, do [B, H, Lq,
+    d_v] in ``out_dtype`` (q's dtype by default) with a contiguous head dim,
+    lse, dlse contiguous float32 [B, H, Lq], all on q's device."""
+    import torch
+    if len(out) != 4:
+        raise ValueError("out must be (o, do, lse, dlse)")
+    o, do, lse, dlse = out
+    B, H, Lq, dv_ = shape.batch, shape.heads, shape.seqlen_q, shape.head_dim_v
+    dt = q.dtype if out_dtype is None else out_dtype
+    for name, t in (("o", o), ("do", do)):
+        check_tensor(t, name, (B, H, Lq, dv_), dt, q.device)
+        _strides3(t)
+    for name, t in (("lse", lse), ("dlse", dlse)):
+        check_tensor(t, name, (B, H, Lq), torch.float32, q.device, contiguous=True)
+    return o, do, lse, dlse
+
+
+def _alloc_fwd_out(q, shape, dtype):
+    import torch
+    B, H, Lq, dv_ = shape.batch, shape.heads, shape.seqlen_q, shape.head_dim_v
+    o = torch.empty((B, H, Lq, dv_), device=q.device, dtype=dtype)
+    do = torch.empty_like(o)
+    lse = torch.empty((B, H, Lq), device=q.device, dtype=torch.float32)
+    dlse = torch.empty_like(lse)
+    return o, do, lse, dlse
+
+
+def fwd(q, k, v, dq, dk, dv, scale=None, mask=None, out=None):
+    """(o, do, lse, dlse) for GPU tensors q [B, H, Lq, d_qk], k [B, H, Lkv,
+    d_qk], v [B, H, Lkv, d_v] (bf16 or float32).
+
+    Tangents must have their primal's shape and strides.  ``mask`` is None or
+    a frame-window dict/Mask (self-attention, Lq == Lkv).  Outputs o, do
+    [B, H, Lq, d_v] and lse, dlse [B, H, Lq] are allocated contiguous unless
+    ``out = (o, do, lse, dlse)`` is given.  Runs on the current stream.
+    """
+    import torch
+    dt, shape = check_qkv(q, k, v, dq, dk, dv)
+    o, do, lse, dlse = (_alloc_fwd_out(q, shape, q.dtype) if out is None
+                        else check_fwd_out(out, q, shape))
+    _require_gpu(q, "q")
+    lay = layout_of(q, k, v, dq, dk, dv, o, do)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = attn_jvp_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), dq.data_ptr(),
+                         dk.data_ptr(), dv.data_ptr(), o.data_ptr(), do.data_ptr(),
+                         lse.data_ptr(), dlse.data_ptr(), shape,
+                         0.0 if scale is None else float(scale), dt, lay, mask, stream)
+    if st != 0:
+        raise AttnJvpError(st, "attn_jvp_fwd_ex")
+    return o, do, lse, dlse
+
+
 def fwd_partial(q, k, v, dq, dk, dv, scale=None):
     """float32 partials (o, do, lse, dlse) of the keys given (see
     attn_jvp_fwd_partial): o, do [B, H, Lq, d_v], lse, dlse [B, H, Lq]."""
     import torch
-    dt, shape = _check_qkv(q, k, v, dq, dk, dv)
-    B, H, Lq, dv_ = shape.batch, shape.heads, shape.seqlen_q, shape.head_dim_v
-    o = torch.empty((B, H, Lq, dv_), device=q.device, dtype=torch.float32)
-    do = torch.empty_like(o)
-    lse = torch.empty((B, H, Lq), device=q.device, dtype=torch.float32)
-    dlse = torch.empty_like(lse)
+    dt, shape = check_qkv(q, k, v, dq, dk, dv)
+    _require_gpu(q, "q")
+    o, do, lse, dlse = _alloc_fwd_out(q, shape, torch.float32)
     lay = layout_of(q, k, v, dq, dk, dv, q, dq)     # o / dout strides are ignored
     st = attn_jvp_fwd_partial(q.data_ptr(), k.data_ptr(), v.data_ptr(), dq.data_ptr(),
                               dk.data_ptr(), dv.data_ptr(), o.data_ptr(), do.data_ptr(),
@@ -373,55 +419,77 @@ def fwd_partial(q, k, v, dq, dk, dv, scale=None):
     return o, do, lse, dlse
 
 
+def check_merge(o_parts, do_parts, lse_parts, dlse_parts, dtype, out=None):
+    """Validate a merge call; returns (P, Shape, out tensors or None)."""
+    import torch
+    if dtype not in _torch_dtypes():
+        raise TypeError(f"unsupported output dtype {dtype}")
+    if o_parts.dim() != 5:
+        raise ValueError("o_parts must be [P, B, H, Lq, d_v]")
+    P, B, H, Lq, dv_ = o_parts.shape
+    dev = o_parts.device
+    check_tensor(o_parts, "o_parts", (P, B, H, Lq, dv_), torch.float32, dev, contiguous=True)
+    check_tensor(do_parts, "do_parts", (P, B, H, Lq, dv_), torch.float32, dev, contiguous=True)
+    check_tensor(lse_parts, "lse_parts", (P, B, H, Lq), torch.float32, dev, contiguous=True)
+    check_tensor(dlse_parts, "dlse_parts", (P, B, H, Lq), torch.float32, dev, contiguous=True)
+    shape = Shape(B, H, Lq, Lq, dv_, dv_)
+    if out is not None:
+        out = check_fwd_out(out, o_parts, shape, out_dtype=dtype)
+    return P, shape, out
+
+
 def merge(o_parts, do_parts, lse_parts, dlse_parts, dtype, out=None):
     """Merge float32 partials stacked on a leading parts axis (o_parts, do_parts
     [P, B, H, Lq, d_v], lse_parts, dlse_parts [P, B, H, Lq], contiguous) into
     (o, do, lse, dlse) with o, do in ``dtype`` (torch.bfloat16/float32)."""
     import torch
-    P, B, H, Lq, dv_ = o_parts.shape
-    for t in (o_parts, do_parts, lse_parts, dlse_parts):
-        if t.dtype != torch.float32 or not t.is_contiguous():
-            raise ValueError("partials must be contiguous float32")
-    if tuple(do_parts.shape) != tuple(o_parts.shape) or tuple(lse_parts.shape) != (P, B, H, Lq) \
-            or tuple(dlse_parts.shape) != (P, B, H, Lq):
-        raise ValueError("inconsistent partial shapes")
-    dt = {torch.bfloat16: ATTN_JVP_BF16, torch.float32: ATTN_JVP_FP32}[dtype]
-    if out is None:
-        o = torch.empty((B, H, Lq, dv_), device=o_parts.device, dtype=dtype)
-        do = torch.empty_like(o)
-        lse = torch.empty((B, H, Lq), device=o_parts.device, dtype=torch.float32)
-        dlse = torch.empty_like(lse)
-    else:
-        o, do, lse, dlse = out
+    P, shape, out = check_merge(o_parts, do_parts, lse_parts, dlse_parts, dtype, out)
+    _require_gpu(o_parts, "o_parts")
+    o, do, lse, dlse = _alloc_fwd_out(o_parts, shape, dtype) if out is None else out
+    B, H, Lq, dv_ = shape.batch, shape.heads, shape.seqlen_q, shape.head_dim_v
     st = attn_jvp_merge(P, o_parts.data_ptr(), do_parts.data_ptr(), lse_parts.data_ptr(),
                         dlse_parts.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
-                        dlse.data_ptr(), B, H, Lq, dv_, dt, _strides3(o),
+                        dlse.data_ptr(), B, H, Lq, dv_, _torch_dtypes()[dtype], _strides3(o),
                         torch.cuda.current_stream(o_parts.device).cuda_stream)
     if st != 0:
         raise AttnJvpError(st, "attn_jvp_merge")
     return o, do, lse, dlse
 
 
+def check_workspace(workspace, need, device):
+    """A caller's split-KV workspace: a contiguous tensor on ``device`` of at
+    least ``need`` bytes."""
+    import torch
+    if not isinstance(workspace, torch.Tensor):
+        raise ValueError("workspace must be a tensor")
+    if workspace.device != device:
+        raise ValueError(f"workspace must be on {device}, got {workspace.device}")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    nbytes = workspace.numel() * workspace.element_size()
+    if nbytes < need:
+        raise ValueError(f"workspace holds {nbytes} bytes, the plan needs {need}")
+    return nbytes
+
+
 def fwd_splitkv(q, k, v, dq, dk, dv, scale=None, mask=None, num_splits=0, workspace=None,
                 out=None):
     """``fwd`` with key splits and a merge (attn_jvp_fwd_splitkv).  The
-    workspace (a CUDA uint8 tensor of at least the plan's size) is allocated
-    with torch.empty when not given.  Returns (o, do, lse, dlse, splits)."""
+    workspace (a GPU tensor of at least the plan's size, on q's device) is
+    allocated with torch.empty when not given.  Returns (o, do, lse, dlse,
+    splits)."""
     import torch
-    dt, shape = _check_qkv(q, k, v, dq, dk, dv)
+    dt, shape = check_qkv(q, k, v, dq, dk, dv)
+    o, do, lse, dlse = (_alloc_fwd_out(q, shape, q.dtype) if out is None
+                        else check_fwd_out(out, q, shape))
+    _require_gpu(q, "q")
     ns, need = attn_jvp_splitkv_plan(shape, dt, mask, num_splits)
-    B, H, Lq, dv_ = shape.batch, shape.heads, shape.seqlen_q, shape.head_dim_v
-    if out is None:
-        o = torch.empty((B, H, Lq, dv_), device=q.device, dtype=q.dtype)
-        do = torch.empty_like(o)
-        lse = torch.empty((B, H, Lq), device=q.device, dtype=torch.float32)
-        dlse = torch.empty_like(lse)
-    else:
-        o, do, lse, dlse = out
     if workspace is None and need:
         workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
-    wp = 0 if workspace is None else workspace.data_ptr()
-    wb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    wp, wb = 0, 0
+    if workspace is not None:
+        wb = check_workspace(workspace, need, q.device)
+        wp = workspace.data_ptr()
     lay = layout_of(q, k, v, dq, dk, dv, o, do)
     st = attn_jvp_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), dq.data_ptr(),
                               dk.data_ptr(), dv.data_ptr(), o.data_ptr(), do.data_ptr(),
@@ -433,6 +501,38 @@ def fwd_splitkv(q, k, v, dq, dk, dv, scale=None, mask=None, num_splits=0, worksp
     return o, do, lse, dlse, ns
 
 
+def check_bwd_args(q, k, v, o, go, lse, out=None):
+    """(dtype code, Shape, out tensors or None) of a backward call; raises on
+    any mismatch of shape, dtype or device, a non-contiguous lse or out
+    tensors of the wrong shape, dtype or device."""
+    import torch
+    dtypes = _torch_dtypes()
+    if q.dtype not in dtypes:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-d [B, H, L, d]")
+    B, H, Lq, d = q.shape
+    Lkv, dv_ = k.shape[2], v.shape[3]
+    if tuple(k.shape) != (B, H, Lkv, d) or tuple(v.shape) != (B, H, Lkv, dv_) \
+            or tuple(o.shape) != (B, H, Lq, dv_) or tuple(go.shape) != (B, H, Lq, dv_):
+        raise ValueError("shapes must be q [B,H,Lq,d], k, v [B,H,Lkv,d], o, go [B,H,Lq,d]")
+    for t in (k, v, o, go):
+        if t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v, o, go must share dtype and device")
+    check_tensor(lse, "lse", (B, H, Lq), torch.float32, q.device, contiguous=True)
+    if out is not None:
+        if len(out) != 4:
+            raise ValueError("out must be (gq, gk, gv, delta)")
+        gq, gk, gv, delta = out
+        check_tensor(gq, "gq", q.shape, q.dtype, q.device)
+        check_tensor(gk, "gk", k.shape, q.dtype, q.device)
+        check_tensor(gv, "gv", v.shape, q.dtype, q.device)
+        check_tensor(delta, "delta", (B, H, Lq), torch.float32, q.device, contiguous=True)
+        for t in (gq, gk, gv):
+            _strides3(t)
+    return dtypes[q.dtype], Shape(B, H, Lq, Lkv, d, dv_), out
+
+
 def bwd(q, k, v, o, go, lse, scale=None, mask=None, out=None):
     """Primal gradients (gq, gk, gv, delta) of a loss with dL/dO = go, for
     q [B, H, Lq, d], k, v [B, H, Lkv, d], o, go [B, H, Lq, d] (bf16 or
@@ -442,32 +542,21 @@ def bwd(q, k, v, o, go, lse, scale=None, mask=None, out=None):
     mask.  Outputs are allocated contiguous unless ``out = (gq, gk, gv,
     delta)`` is given.  Runs on the current stream."""
     import torch
-    dtypes = {torch.bfloat16: ATTN_JVP_BF16, torch.float32: ATTN_JVP_FP32}
-    if q.dtype not in dtypes:
-        raise TypeError(f"unsupported dtype {q.dtype}")
-    B, H, Lq, d = q.shape
-    Lkv = k.shape[2]
-    if tuple(k.shape) != (B, H, Lkv, d) or tuple(v.shape) != (B, H, Lkv, v.shape[3]) \
-            or tuple(o.shape) != (B, H, Lq, v.shape[3]) or go.shape != o.shape:
-        raise ValueError("shapes must be q [B,H,Lq,d], k, v [B,H,Lkv,d], o, go [B,H,Lq,d]")
-    if tuple(lse.shape) != (B, H, Lq) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 [B, H, Lq]")
-    for t in (k, v, o, go):
-        if t.dtype != q.dtype or t.device != q.device:
-            raise ValueError("q, k, v, o, go must share dtype and device")
+    dt, shape, out = check_bwd_args(q, k, v, o, go, lse, out)
+    _require_gpu(q, "q")
     if out is None:
         gq, gk, gv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        delta = torch.empty((B, H, Lq), device=q.device, dtype=torch.float32)
+        delta = torch.empty((shape.batch, shape.heads, shape.seqlen_q), device=q.device,
+                            dtype=torch.float32)
     else:
         gq, gk, gv, delta = out
     lay = BwdLayout()
     for name, t in zip(("q", "k", "v", "o", "go", "gq", "gk", "gv"), (q, k, v, o, go, gq, gk, gv)):
         getattr(lay, name)[:] = _strides3(t)
-    shape = Shape(B, H, Lq, Lkv, d, v.shape[3])
     st = attn_jvp_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), go.data_ptr(),
                       lse.data_ptr(), gq.data_ptr(), gk.data_ptr(), gv.data_ptr(),
                       delta.data_ptr(), shape, 0.0 if scale is None else float(scale),
-                      dtypes[q.dtype], lay, mask, torch.cuda.current_stream(q.device).cuda_stream)
+                      dt, lay, mask, torch.cuda.current_stream(q.device).cuda_stream)
     if st != 0:
         raise AttnJvpError(st, "attn_jvp_bwd")
     return gq, gk, gv, delta

@@ -37,63 +37,6 @@
 
 namespace attn_jvp {
 
-struct BwdParams {
-  const void *q, *k, *v, *o, *g;   // inputs; g = dL/dO
-  const float *lse;                // [B, H, Nq], natural log, from the forward
-  void *gq, *gk, *gv;              // outputs dL/dQ, dL/dK, dL/dV
-  float *delta;                    // [B, H, Nq]: D = rowsum(G (.) O), written by the dQ kernel
-  int64_t sq[3], sk[3], sv[3], so[3], sg[3], sgq[3], sgk[3], sgv[3];   // (b, h, n) strides
-  int B, H, Nq, Nkv;
-  int nqb, nkb;                    // query / key blocks per (b, h)
-  float scale, scale_log2;
-  MaskDev mask;                    // frame window (kind 0: none); Nq == Nkv when on
-  int rbq, rbk;                    // 16-row blocks per dQ / dK-dV wave (1, or 2 where built)
-};
-
-// Query-tile ranges [lo, hi) that see some key of rows [k_lo, k_hi) under the
-// frame window: the transpose of visible_tiles.  A block holding a key of an
-// anchor frame is seen by every query; otherwise the queries of the chunks
-// within the radius of the block's chunks, plus (anchor_queries_see_all) the
-// anchor query frames.
-__host__ __device__ inline TileRanges visible_query_tiles(const MaskDev &m, int k_lo, int k_hi,
-                                                          int N, int BN) {
-  TileRanges tr;
-  const int ntiles = (N + BN - 1) / BN;
-  tr.n = 1;
-  tr.lo[0] = 0;
-  tr.hi[0] = ntiles;
-  tr.lo[1] = tr.hi[1] = tr.lo[2] = tr.hi[2] = 0;
-  if (m.kind == 0) return tr;
-  const int T = m.tpf, C = m.chunk, F = m.frames, R = m.radius;
-  const int kf0 = k_lo / T, kf1 = (k_hi - 1) / T;
-  if ((m.first && kf0 == 0) || (m.last && kf1 == F - 1)) return tr;
-  const int c0 = kf0 / C, c1 = kf1 / C;
-  const long long f_lo_l = (long long)(c0 - R) * C;
-  const int f_lo = f_lo_l < 0 ? 0 : (int)f_lo_l;
-  const long long f_hi_l = (long long)(c1 + R + 1) * C;
-  const int f_hi = f_hi_l > F ? F : (int)f_hi_l;
-  tr.n = 0;
-  tr.lo[0] = tr.hi[0] = 0;
-  const bool valid[3] = {m.see_all && m.first, true, m.see_all && m.last};
-  const int a_[3] = {0, f_lo * T / BN, (F - 1) * T / BN};
-  const int z_[3] = {(T + BN - 1) / BN, (f_hi * T + BN - 1) / BN, (F * T + BN - 1) / BN};
-#pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    if (!valid[i]) continue;
-    const int a = a_[i], z = z_[i];
-    if (tr.n == 0) {
-      tr.lo[0] = a; tr.hi[0] = z; tr.n = 1;
-    } else if (tr.n == 1) {
-      if (a <= tr.hi[0]) tr.hi[0] = z > tr.hi[0] ? z : tr.hi[0];
-      else { tr.lo[1] = a; tr.hi[1] = z; tr.n = 2; }
-    } else {
-      if (a <= tr.hi[1]) tr.hi[1] = z > tr.hi[1] ? z : tr.hi[1];
-      else { tr.lo[2] = a; tr.hi[2] = z; tr.n = 3; }
-    }
-  }
-  return tr;
-}
-
 // Global->LDS copies of the streamed tiles: SideCopier's scheme (1 KiB per
 // wave instruction, lane-chosen swizzled chunk, clamped tail rows) for two
 // tensors with their own row strides; KS is the swizzle kind of lds_off.
@@ -169,32 +112,15 @@ template <typename T, int D>
 struct BwdCfg {
   static constexpr int ES = (int)sizeof(T);
   static constexpr int RB = D * ES;
-  // resident per lane: two operand fragment sets and one (dQ) or two (dK,
-  // dV) accumulator sets
-  static constexpr int kResDq = (ES == 2 ? D / 4 : D / 2) + D / 4;
-  static constexpr int kResDkv = (ES == 2 ? D / 4 : D / 2) + D / 2;
-  // bf16 d = 64 dQ: four waves (of up to two row blocks), two workgroups
-  // per CU (4 % faster at the prefix shape than eight waves)
-  static constexpr int kWavesDq = (ES == 2 && D == 64) ? 4 : (kResDq <= 96 ? 8 : 4);
-  static constexpr int kMinBlocksDq = (ES == 2 && D == 64) ? 2 : 1;
-  // bfloat16 d = 128 and d = 64 dQ waves may own two 16-row blocks (the
-  // resident set stays within 128 VGPRs): every streamed LDS fragment then
-  // feeds both blocks, halving the LDS bytes per MFMA of the LDS-bound launch
-  static constexpr int kRbDqMax = (ES == 2 && (D == 128 || D == 64)) ? 2 : 1;
-  // the same for the key-owned launch: at d = 64 (96 resident VGPRs for two
-  // blocks, two waves per SIMD) and at d = 128 (192 resident, four waves)
-  static constexpr int kRbDkvMax = (ES == 2 && (D == 64 || D == 128)) ? 2 : 1;
-  // bf16 d = 128 and d = 64 dK/dV: four waves of two 16-row blocks each
-  // (d = 128: the registers of one wave per SIMD; d = 64: two such
-  // workgroups per CU); 5-9 % faster than eight waves of one block
-  static constexpr int kWavesDkv =
-      (ES == 2 && (D == 128 || D == 64)) ? 4 : (kResDkv <= (ES == 2 ? 96 : 48) ? 8 : 4);
-  static constexpr int kMinBlocksDkv = (ES == 2 && D == 64) ? 2 : 1;
-  // 64-row tiles while two stages of both tensors fit in 128 KiB and the
-  // transposing reads' largest constant offset (stage, second tensor, row
-  // 48 of the tile) fits the 16-bit DS offset field; else 32
-  static constexpr int kBN = (4 * 64 * RB <= 128 * 1024 && 3 * 64 * RB + 48 * RB < 65536) ? 64 : 32;
-  static constexpr int kLds = 4 * kBN * RB;                         // 2 stages x 2 tensors
+  static constexpr BwdGeom G = bwd_geom(ES, D);
+  static constexpr int kWavesDq = G.waves_dq;
+  static constexpr int kMinBlocksDq = G.min_blocks_dq;
+  static constexpr int kRbDqMax = G.rb_dq_max;
+  static constexpr int kWavesDkv = G.waves_dkv;
+  static constexpr int kMinBlocksDkv = G.min_blocks_dkv;
+  static constexpr int kRbDkvMax = G.rb_dkv_max;
+  static constexpr int kBN = G.block_n;
+  static constexpr int kLds = G.lds;   // 2 stages x 2 tensors
 };
 
 template <typename T, int D, bool KEYS, bool MASKED, int RBS>
@@ -282,12 +208,9 @@ void bwd_kernel(BwdParams p) {
     tr = KEYS ? visible_query_tiles(p.mask, r0, r_hi, Nq, BN)
               : visible_tiles(p.mask, r0, r_hi, Nkv, BN);
   } else {
-    tr.n = 1;
-    tr.lo[0] = 0;
-    tr.hi[0] = (Nstr + BN - 1) / BN;
-    tr.lo[1] = tr.hi[1] = tr.lo[2] = tr.hi[2] = 0;
+    tr = all_tiles(Nstr, BN);
   }
-  const int ntile = (tr.hi[0] - tr.lo[0]) + (tr.hi[1] - tr.lo[1]) + (tr.hi[2] - tr.lo[2]);
+  const int ntile = tile_count(tr);
 
   // Mask terms.  The lane's own row sees the streamed rows [vis_lo, vis_hi)
   // by the chunk rule, plus [0, a_first_hi) and [a_last_lo, Nstr) (anchor

@@ -56,6 +56,8 @@
 
 #include <type_traits>
 
+#include "plan.h"
+
 namespace attn_jvp {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -75,21 +77,13 @@ struct Cfg {
   static constexpr int ES = (int)sizeof(T);
   static constexpr int RBK = DQK * ES;   // bytes per K / dK row
   static constexpr int RBV = DV * ES;    // bytes per V / dV row
-  // VGPRs per lane that stay resident: Q and dQ fragments, O, A, B blocks.
-  // Two waves per SIMD (256 VGPRs each) while they leave room for the step's
-  // working set; float32 score steps need more of it (one k-step per 4 d).
-  // bfloat16 d_qk = d_v = 64 (152 VGPRs) runs three waves per SIMD: its
-  // softmax VALU work per MFMA is twice that of d = 128, and a third wave
-  // per SIMD keeps the matrix cores fed (measured 7-12 % faster per
-  // workgroup; at d = 16 and 32 a third wave was slower).
-  static constexpr int kResident = (ES == 2 ? DQK / 4 : DQK / 2) + 3 * DV / 4;
-  static constexpr int kWaves = (ES == 2 && DQK == 64 && DV == 64)
-                                    ? 12
-                                    : (kResident <= (ES == 2 ? 128 : 64) ? 8 : 4);
+  static constexpr FwdGeom G = fwd_geom(ES, DQK, DV);
+  static constexpr int kWaves = G.waves;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kBlockM = kWaveRows * kWaves;
-  static constexpr int kBN = 4 * 64 * (RBK + RBV) <= 128 * 1024 ? 64 : 32;
-  static constexpr int kLds = 4 * kBN * (RBK + RBV);   // two stages of K, dK, V, dV
+  static constexpr int kBlockM = G.block_m;
+  static constexpr int kBN = G.block_n;
+  static constexpr int kLds = G.lds;   // two stages of K, dK, V, dV
+  static_assert(kBlockM == kWaveRows * kWaves, "16 query rows per wave");
 };
 
 // ---------------------------------------------------------------------------
@@ -141,90 +135,6 @@ template <> struct ElemV<float> {
   __device__ static inline f32x4 mfma(Frag a, Frag b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
   }
-};
-
-// ---------------------------------------------------------------------------
-// Frame-window mask (page "VDN-Minimax-H3 ... Stage A1", yfxerp.com).
-// ---------------------------------------------------------------------------
-struct MaskDev {
-  int kind;        // 0 none, 1 frame window
-  int frames, tpf, chunk, radius;
-  int first, last, see_all;
-  float inv_tpf, inv_chunk;
-};
-
-// floor(n / den) for 0 <= n < 2^24 from a float estimate and exact fix-up.
-__host__ __device__ inline int div_fix(int n, int den, float inv) {
-  int q = (int)((float)n * inv);
-  q -= (q * den > n);
-  q -= (q * den > n);
-  q += ((q + 1) * den <= n);
-  q += ((q + 1) * den <= n);
-  return q;
-}
-
-struct TileRanges {
-  int n;
-  int lo[3], hi[3];   // key-tile index ranges [lo, hi), ascending, disjoint
-};
-
-// Key-tile ranges that some query of rows [q_lo, q_hi) can see.
-__host__ __device__ inline TileRanges visible_tiles(const MaskDev &m, int q_lo,
-                                                    int q_hi, int N, int BN) {
-  TileRanges tr;
-  const int ntiles = (N + BN - 1) / BN;
-  tr.n = 1;
-  tr.lo[0] = 0;
-  tr.hi[0] = ntiles;
-  tr.lo[1] = tr.hi[1] = tr.lo[2] = tr.hi[2] = 0;
-  if (m.kind == 0) return tr;
-  const int T = m.tpf, C = m.chunk, F = m.frames, R = m.radius;
-  const int qf0 = q_lo / T, qf1 = (q_hi - 1) / T;
-  if (m.see_all && ((m.first && qf0 == 0) || (m.last && qf1 == F - 1))) return tr;
-  const int c0 = qf0 / C, c1 = qf1 / C;
-  long long f_lo_l = (long long)(c0 - R) * C;
-  const int f_lo = f_lo_l < 0 ? 0 : (int)f_lo_l;
-  long long f_hi_l = (long long)(c1 + R + 1) * C;
-  int f_hi = f_hi_l > F ? F : (int)f_hi_l;
-  // candidate key-tile intervals in ascending order of start: first-frame
-  // anchor, chunk window, last-frame anchor; merged where they touch
-  // (static indices only, so nothing is spilled to memory)
-  tr.n = 0;
-  tr.lo[0] = tr.hi[0] = tr.lo[1] = tr.hi[1] = tr.lo[2] = tr.hi[2] = 0;
-  const bool valid[3] = {m.first != 0, true, m.last != 0};
-  const int a_[3] = {0, f_lo * T / BN, (F - 1) * T / BN};
-  const int z_[3] = {(T + BN - 1) / BN, (f_hi * T + BN - 1) / BN, (F * T + BN - 1) / BN};
-#pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    if (!valid[i]) continue;
-    const int a = a_[i], z = z_[i];
-    if (tr.n == 0) {
-      tr.lo[0] = a; tr.hi[0] = z; tr.n = 1;
-    } else if (tr.n == 1) {
-      if (a <= tr.hi[0]) tr.hi[0] = z > tr.hi[0] ? z : tr.hi[0];
-      else { tr.lo[1] = a; tr.hi[1] = z; tr.n = 2; }
-    } else {
-      if (a <= tr.hi[1]) tr.hi[1] = z > tr.hi[1] ? z : tr.hi[1];
-      else { tr.lo[2] = a; tr.hi[2] = z; tr.n = 3; }
-    }
-  }
-  return tr;
-}
-
-// ---------------------------------------------------------------------------
-// Kernel parameters.
-// ---------------------------------------------------------------------------
-struct Params {
-  const void *q, *k, *v, *dq, *dk, *dv;
-  void *o, *dout;
-  float *lse, *dlse;
-  int64_t sq[3], sk[3], sv[3], so[3];   // (b, h, n) element strides
-  int B, H, Nq, Nkv;
-  int nqb;                              // query blocks per (b, h)
-  int nsplit;                           // key splits per query block (1: none)
-  int partial;                          // 1: outputs are float32 partials
-  float scale, scale_log2;
-  MaskDev mask;
 };
 
 __device__ inline int logical_block_id() {
@@ -447,16 +357,6 @@ __device__ inline void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
-// Tile index of the idx-th visited tile.
-__device__ inline int tile_at(const TileRanges &tr, int idx) {
-  int t = tr.lo[0] + idx;
-  if (tr.n > 1 && t >= tr.hi[0]) {
-    t = tr.lo[1] + (t - tr.hi[0]);
-    if (tr.n > 2 && t >= tr.hi[1]) t = tr.lo[2] + (t - tr.hi[1]);
-  }
-  return t;
-}
-
 // Lazy rescale: the running max only moves when a step's max exceeds it by
 // more than 2^8 (P~ then stays below 256); the final normalisation uses the
 // same reference, so the result is unchanged.
@@ -510,17 +410,11 @@ __global__ __launch_bounds__((Cfg<T, DQK, DV>::kThreads), 1) void attn_jvp_kerne
   const int q_hi = (q0 + C::kBlockM < Nq) ? q0 + C::kBlockM : Nq;
 
   TileRanges tr;
-  if constexpr (MASKED) {
-    tr = visible_tiles(p.mask, q0, q_hi, Nkv, BN);
-  } else {
-    tr.n = 1;
-    tr.lo[0] = 0;
-    tr.hi[0] = (Nkv + BN - 1) / BN;
-    tr.lo[1] = tr.hi[1] = tr.lo[2] = tr.hi[2] = 0;
-  }
+  if constexpr (MASKED) tr = visible_tiles(p.mask, q0, q_hi, Nkv, BN);
+  else tr = all_tiles(Nkv, BN);
   // unused ranges are empty (lo = hi = 0).  With key splits, this workgroup
   // takes the split-th run of ceil(n / nsplit) of the n visited tiles.
-  const int nvis = (tr.hi[0] - tr.lo[0]) + (tr.hi[1] - tr.lo[1]) + (tr.hi[2] - tr.lo[2]);
+  const int nvis = tile_count(tr);
   const int per_split = (nvis + p.nsplit - 1) / p.nsplit;
   const int t_first = split * per_split;
   const int t_last = t_first + per_split < nvis ? t_first + per_split : nvis;
@@ -963,17 +857,6 @@ hipError_t launch_instance(const Params &p, hipStream_t stream) {
   hipLaunchKernelGGL((attn_jvp_kernel<T, DQK, DV, MASKED>), dim3(grid), dim3(C::kThreads), 0,
                      stream, p);
   return hipGetLastError();
-}
-
-// Launch shape of (T, d_qk, d_v) for the host.
-struct Shape {
-  int waves, block_m, block_n;
-};
-
-template <typename T, int DQK, int DV>
-Shape shape_of() {
-  using C = Cfg<T, DQK, DV>;
-  return Shape{C::kWaves, C::kBlockM, C::kBN};
 }
 
 }  // namespace attn_jvp

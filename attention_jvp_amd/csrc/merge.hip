@@ -25,9 +25,9 @@ namespace attn_jvp {
 namespace {
 
 template <typename T>
-__global__ __launch_bounds__(256) void merge_kernel(MergeParams m) {
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams m) {
   const int cpr = m.dv / 4;                               // threads per row
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t t = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
   const int64_t rows = (int64_t)m.B * m.H * m.Nq;
   if (t >= rows * cpr) return;
   const int64_t row = t / cpr;
@@ -113,12 +113,12 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams m) {
 
 hipError_t launch_merge(const MergeParams &m, bool bf16, hipStream_t s) {
   const int64_t threads = (int64_t)m.B * m.H * m.Nq * (m.dv / 4);
-  const int64_t blocks = (threads + 255) / 256;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  const int64_t blocks = (threads + kMergeThreads - 1) / kMergeThreads;
+  if (blocks > 0x7fffffffLL || blocks * kMergeThreads > 0xffffffffLL) return hipErrorInvalidValue;
   if (bf16)
-    hipLaunchKernelGGL(merge_kernel<__bf16>, dim3((unsigned)blocks), dim3(256), 0, s, m);
+    hipLaunchKernelGGL(merge_kernel<__bf16>, dim3((unsigned)blocks), dim3(kMergeThreads), 0, s, m);
   else
-    hipLaunchKernelGGL(merge_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, s, m);
+    hipLaunchKernelGGL(merge_kernel<float>, dim3((unsigned)blocks), dim3(kMergeThreads), 0, s, m);
   return hipGetLastError();
 }
 

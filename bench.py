@@ -71,11 +71,12 @@ def visible_pairs(N, mask):
 
 def kernel_sha():
     """sha256 over the sources of the forward attention kernel itself: the
-    template (kernel.h) and its instance units (inst.h, inst_bf16_*.hip,
-    inst_fp32.hip), by name."""
+    template (kernel.h), its launch geometry (plan.h) and its instance units
+    (inst.h, inst_bf16_*.hip, inst_fp32.hip), by name."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(KERNEL_SOURCES)):
-        if name in ("kernel.h", "inst.h", "inst_fp32.hip") or name.startswith("inst_bf16_"):
+        if name in ("kernel.h", "plan.h", "inst.h", "inst_fp32.hip") or \
+                name.startswith("inst_bf16_"):
             h.update(name.encode())
             with open(os.path.join(KERNEL_SOURCES, name), "rb") as f:
                 h.update(f.read())
@@ -106,8 +107,11 @@ def blas_threads():
     return len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(w, x, target_s):
-    """Time the float64 oracle on a bounded row sample of the same workload."""
+def cpu_baseline(w, x, target_s, gpu_out=None):
+    """Time the float64 oracle on a bounded row sample of the same workload,
+    and (with gpu_out, the outputs of a timed launch) compare the GPU's rows
+    of that sample with the oracle's: normwise error of O, dO, dLSE and the
+    absolute error of LSE in nats."""
     import numpy as np
     from oracle import FrameWindow, attention_jvp_rows
 
@@ -122,30 +126,45 @@ def cpu_baseline(w, x, target_s):
     def run(nrows):
         rows = np.linspace(0, w.N - 1, nrows).astype(np.int64)
         t0 = time.perf_counter()
-        attention_jvp_rows(*arrs, rows, visible=vis)
-        return time.perf_counter() - t0, rows
+        ref = attention_jvp_rows(*arrs, rows, visible=vis)
+        return time.perf_counter() - t0, rows, ref
 
     # calibrate t(n) = fixed + n * per_row from two short runs (the fixed
     # part is the per-head widening of K, V, dK, dV to float64)
-    t16, _ = run(16)
-    t64, _ = run(64)
+    t16, _, _ = run(16)
+    t64, _, _ = run(64)
     per_row = max((t64 - t16) / 48, 1e-9)
     fixed = max(t16 - 16 * per_row, 0.0)
     nrows = int(max(16, min(w.N, (target_s - fixed) / per_row)))
-    dt, rows = run(nrows)
+    dt, rows, ref = run(nrows)
     if vis is None:
         pairs = len(rows) * w.Nkv
     else:
         pairs = int(vis(rows, np.arange(w.Nkv)).sum())
     flops = 6.0 * w.B * w.H * pairs * (w.d + w.dv)
+    parity = None
+    if gpu_out is not None:
+        import torch
+        idx = torch.from_numpy(rows).to(gpu_out[0].device)
+        got = [t.index_select(2, idx).double().cpu().numpy() for t in gpu_out]
+        parity = {"rows_per_head": int(len(rows))}
+        for name, g, r in zip(("O", "dO", "LSE", "dLSE"), got, ref):
+            fin = np.isfinite(r)
+            diff = float(np.max(np.abs(g[fin] - r[fin]))) if fin.any() else 0.0
+            if name == "LSE":
+                parity["LSE_abs_nats"] = diff
+            else:
+                den = float(np.max(np.abs(r[fin]))) if fin.any() else 1.0
+                parity[name + "_normwise"] = diff / max(den, 1e-30)
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": blas_threads(),
+        "affinity_cores": len(os.sched_getaffinity(0)),
         "kind": "oracle",
         "sample": (f"{len(rows)} evenly spaced query rows x {w.B * w.H} heads of {w.name} "
                    f"against all {w.Nkv} keys, float64 numpy; {dt:.1f} s"),
-    }
+    }, parity
 
 
 def main():
@@ -284,11 +303,11 @@ def main():
     peak = PEAK_TFLOPS[w.dtype]
     log(f"{ms:.4f} ms/step, {tflops:.1f} TFLOP/s ({100 * tflops / peak:.1f}% of {peak} peak)")
 
-    cpu = None
+    cpu = parity = None
     if not args.no_cpu_baseline and not args.backward:
-        log("timing the float64 oracle on a row sample")
-        cpu = cpu_baseline(w, x, args.cpu_seconds)
-        log(f"oracle: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads")
+        log("timing the float64 oracle on a row sample (and checking the GPU's rows of it)")
+        cpu, parity = cpu_baseline(w, x, args.cpu_seconds, gpu_out=outs)
+        log(f"oracle: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads; parity {parity}")
 
     line = {
         "metric": METRIC if not args.backward else
@@ -307,7 +326,7 @@ def main():
         "data": "synthetic",
         "pct_of_peak": round(100 * tflops / peak, 2),
         "config": {
-            "workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+            "workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "seed": w.seed,
             **({"Lkv": w.Nkv, "d_v": w.dv} if (w.Nkv != w.N or w.dv != w.d) else {}),
             **({"splitkv": splits} if splits is not None else {}),
             **({"pass": "backward"} if args.backward else {}),
@@ -323,6 +342,7 @@ def main():
             "traffic": traffic_record(w.name) if splits is None and not args.backward else None,
         },
         "cpu_baseline": cpu,
+        "parity": parity,
         "timing": timing,
     }
     print(json.dumps(line), flush=True)

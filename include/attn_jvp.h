@@ -298,6 +298,11 @@ int attn_jvp_bwd_visible_tiles(int N, int block_rows, int tile_rows, int keys,
 /* Static English text for a status code. */
 const char *attn_jvp_status_string(int status);
 
+/* Host-only: a static NUL-terminated hex string, the sha256 digest of the
+ * sources and compiler flags this library was built from.  A loader compares
+ * it with the digest of the sources beside it and refuses a stale build. */
+const char *attn_jvp_build_id(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -307,3 +307,17 @@ def test_bwd_check():
                                  0, None, win) == -4                          # Lq != Lkv
     bad = aj.Mask.frame_window(frames=6, tokens_per_frame=40, chunk_frames=2, radius_chunks=1)
     assert aj.attn_jvp_bwd_check(*ps, sq, 0, None, bad) == -4                 # 240 tokens != 200
+
+
+def test_library_matches_its_sources(monkeypatch):
+    # the loaded library carries the digest of the sources it was built from
+    import attention_jvp_amd.build as build
+    lib = aj.load()
+    assert lib.attn_jvp_build_id().decode() == build.source_digest()
+    # a library older than the sources beside it is refused
+    monkeypatch.setattr(build, "source_digest", lambda: "0" * 64)
+    monkeypatch.setattr(aj, "_lib", None)
+    with pytest.raises(ImportError, match="other sources"):
+        aj.load()
+    monkeypatch.undo()
+    assert aj.load() is lib or aj.load() is not None

@@ -1,12 +1,12 @@
 """GPU parity for the primal backward (attn_jvp_bwd): dQ, dK, dV of a loss
 with upstream gradient G = dL/dO, from the row log-sum-exp the forward
-stored.  Reference: the float64 oracle backward (every element).  Tolerance:
-normwise max|gpu - ref| / max|ref| <= 2e-2 (bf16) and 1e-4 (float32) per
-output, where for dQ and dK the denominator is at least max|dV_ref| (with a
-single key, or a single visible key per row, the exact dQ and dK are 0 and
-the kernel returns rounding noise of dP - D; dV = P^T G carries the scale of
-the gradients); D = rowsum(G . O) is checked against the same O the kernel
-read.
+stored.  Reference: the float64 oracle backward (every element).  Bounds
+(tests/tolerances.py): normwise max|gpu - ref| / max|ref| of each output
+within the contract (2e-2 bf16, 1e-4 float32) and the regression ceiling.
+Only where the exact dQ and dK are zero (a single key) are their errors
+measured against max|dV_ref| instead, the test asserting that the exact
+values are zero.  D = rowsum(G . O) is checked against the same O the
+kernel read.
 """
 
 import numpy as np
@@ -16,19 +16,12 @@ import torch
 import attention_jvp_amd as aj
 from oracle import FrameWindow, attention_backward, attention_jvp
 from synth import Workload, make_inputs, to_float64
+from tolerances import compare_bwd, normwise, say
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"bf16": 2e-2, "fp32": 1e-4}
 NAMES = ("q", "k", "v", "dq", "dk", "dv")
-
-
-def _say(*a):
-    print(*a, flush=True)
-
-
-def _err(got, ref, floor=0.0):
-    return float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), floor, 1e-30))
+_say = say
 
 
 def _grad_input(w, seed):
@@ -52,13 +45,10 @@ def _check(w, scale=None, from_oracle=False, what=""):
     torch.cuda.synchronize()
     ref = attention_backward(to_float64(x["q"]), to_float64(x["k"]), to_float64(x["v"]),
                              to_float64(g_cpu), scale=scale)
-    errs = {}
-    floor = float(np.max(np.abs(ref[2])))
-    for n, a, r in zip(("dQ", "dK", "dV"), (gq, gk, gv), ref):
-        errs[n] = _err(to_float64(a), r, floor)
-        assert errs[n] <= TOL[w.dtype], f"{what}: {n} normwise error {errs[n]:.3e}"
+    errs = compare_bwd([to_float64(t) for t in (gq, gk, gv)], ref, w.dtype, what,
+                       zero_dq_dk=(w.Nkv == 1))
     d_ref = (to_float64(g_cpu) * to_float64(o)).sum(-1)
-    errs["D"] = _err(to_float64(delta), d_ref)
+    errs["D"] = normwise(to_float64(delta), d_ref)
     assert errs["D"] <= 1e-5, f"{what}: D error {errs['D']:.3e}"
     _say(what, " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
 
@@ -117,12 +107,8 @@ def test_backward_rows_without_keys(dtype, d, Nq, Nkv):
     torch.cuda.synchronize()
     ref = attention_backward(to_float64(x["q"]), to_float64(x["k"]), to_float64(x["v"]),
                              to_float64(g_cpu), visible=vis)
-    errs = {}
-    for n, a, r in zip(("dQ", "dK", "dV"), (gq, gk, gv), ref):
-        a64 = to_float64(a)
-        assert np.isfinite(a64).all(), f"{n} not finite"
-        errs[n] = _err(a64, r)
-        assert errs[n] <= TOL[dtype], f"{n} normwise error {errs[n]:.3e}"
+    errs = compare_bwd([to_float64(t) for t in (gq, gk, gv)], ref, dtype,
+                       f"bwd rows without keys {dtype} d{d}")
     assert np.all(to_float64(gq)[:, :, empty] == 0.0)
     _say(f"bwd rows without keys {dtype} d{d}", " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
 
@@ -146,9 +132,7 @@ def test_backward_strided_bshd_views():
     assert gq.stride() == q.stride() and gk.stride() == k.stride()
     ref = attention_backward(to_float64(x["q"]), to_float64(x["k"]), to_float64(x["v"]),
                              to_float64(g_cpu))
-    errs = {n: _err(to_float64(a), r) for n, a, r in zip(("dQ", "dK", "dV"), (gq, gk, gv), ref)}
-    for n, e in errs.items():
-        assert e <= TOL["bf16"], f"bshd {n} normwise error {e:.3e}"
+    errs = compare_bwd([to_float64(t) for t in (gq, gk, gv)], ref, "bf16", "bwd bshd")
     _say("bwd bshd", " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
 
 
@@ -181,11 +165,7 @@ def test_backward_frame_window(F, T, C, R, first, last, see_all, dtype, d):
     torch.cuda.synchronize()
     ref = attention_backward(to_float64(x["q"]), to_float64(x["k"]), to_float64(x["v"]),
                              to_float64(g_cpu), visible=vis)
-    floor = float(np.max(np.abs(ref[2])))
-    errs = {}
-    for n, a, r in zip(("dQ", "dK", "dV"), (gq, gk, gv), ref):
-        errs[n] = _err(to_float64(a), r, floor)
-        assert errs[n] <= TOL[dtype], f"{what}: {n} normwise error {errs[n]:.3e}"
+    errs = compare_bwd([to_float64(t) for t in (gq, gk, gv)], ref, dtype, what)
     _say(what, " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
 
 
@@ -223,10 +203,7 @@ def test_backward_two_row_blocks_frame_window(d):
     torch.cuda.synchronize()
     ref = attention_backward(to_float64(x["q"]), to_float64(x["k"]), to_float64(x["v"]),
                              to_float64(g_cpu), visible=vis)
-    floor = float(np.max(np.abs(ref[2])))
-    for n, a, r in zip(("dQ", "dK", "dV"), (gq, gk, gv), ref):
-        e = _err(to_float64(a), r, floor)
-        assert e <= TOL["bf16"], f"two row blocks d{d}, mask: {n} normwise error {e:.3e}"
+    compare_bwd([to_float64(t) for t in (gq, gk, gv)], ref, "bf16", f"two row blocks d{d}, mask")
 
 
 def test_backward_deterministic():

@@ -1,8 +1,9 @@
 """GPU parity: the HIP path (through the C-ABI) against the float64 oracle.
 
-Tolerances (stated for the path): float32 inputs, normwise
-max|gpu - ref| / max|ref| <= 1e-5 for O (and LSE) and <= 1e-4 for dO (and
-dLSE); bf16 inputs, the same normwise error <= 2e-2 for every output.  Small
+Bounds (tests/tolerances.py): the contract (normwise max|gpu - ref| /
+max|ref| <= 1e-5 for O and 1e-4 for dO with float32 inputs, 2e-2 with
+bfloat16), a tighter regression ceiling from the path's error model, and an
+absolute bound in nats on LSE.  Small
 shapes are compared element by element on every row; the full-size workloads
 on a deterministic row sample, in the launch configuration the benchmark
 times.
@@ -18,15 +19,12 @@ import torch
 import attention_jvp_amd as aj
 from oracle import FrameWindow, attention_jvp, attention_jvp_rows
 from synth import WORKLOADS, Workload, make_inputs, sample_rows, to_float64
+from tolerances import compare_bwd, compare_fwd, say
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"fp32": (1e-5, 1e-4), "bf16": (2e-2, 2e-2)}
 NAMES = ("q", "k", "v", "dq", "dk", "dv")
-
-
-def _say(*a):
-    print(*a, flush=True)
+_say = say
 
 
 def _dev(x):
@@ -40,29 +38,11 @@ def _run(x, mask=None, scale=None):
     return out
 
 
-def _err(got, ref):
-    den = np.max(np.abs(ref[np.isfinite(ref)])) if np.isfinite(ref).any() else 1.0
-    return float(np.max(np.abs(got - ref)) / max(den, 1e-30))
+def _compare(gpu, ref, dtype, what, **kw):
+    return compare_fwd(gpu, ref, dtype, what, **kw)
 
 
-def _compare(gpu, ref, dtype, what):
-    tol_o, tol_do = TOL[dtype]
-    names = ("O", "dO", "LSE", "dLSE")
-    tols = (tol_o, tol_do, tol_o, tol_do)
-    errs = {}
-    for n, g, r, t in zip(names, gpu, ref, tols):
-        assert np.array_equal(np.isfinite(g), np.isfinite(r)), f"{what}: {n} finiteness"
-        fin = np.isfinite(r)
-        if n == "LSE":
-            assert np.array_equal(g[~fin], r[~fin]), f"{what}: LSE -inf rows"
-        e = _err(g[fin], r[fin]) if fin.any() else 0.0
-        errs[n] = e
-        assert e <= t, f"{what}: {n} normwise error {e:.3e} > {t:.0e}"
-    _say(what, " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
-    return errs
-
-
-def _full_check(w, mask=None, scale=None, seed=None):
+def _full_check(w, mask=None, scale=None, seed=None, **kw):
     x = make_inputs(w, seed=seed)
     mask = x["mask"] if mask is None else mask
     out = _run(x, mask=mask, scale=scale)
@@ -70,7 +50,7 @@ def _full_check(w, mask=None, scale=None, seed=None):
     vis = None if mask is None else FrameWindow(**{k: bool(v) if k.startswith("anchor") else v
                                                    for k, v in mask.items()})
     ref = attention_jvp(*(to_float64(x[n]) for n in NAMES), scale=scale, visible=vis)
-    return _compare(gpu, ref, w.dtype, f"{w.name} B{w.B} H{w.H} N{w.N} d{w.d}")
+    return _compare(gpu, ref, w.dtype, f"{w.name} B{w.B} H{w.H} N{w.N} d{w.d}", **kw)
 
 
 # ---- small shapes: every row, several tiles, ragged tails -----------------
@@ -106,9 +86,11 @@ def test_small_trigflow_and_rms_recipe():
 
 
 def test_large_logits_bf16():
-    # scores of magnitude ~ 30: the running max and rescaling matter
+    # scores of magnitude up to ~100: the running max and rescaling matter;
+    # float32 scores that large carry absolute rounding errors about 30x
+    # those of unit-size scores, so LSE gets a 1e-3 nat bound here
     w = Workload("big", 1, 2, 400, 64, "bf16", 8, tangent_scale=0.1)
-    _full_check(w, scale=4.0)
+    _full_check(w, scale=4.0, lse_abs=1e-3)
 
 
 @pytest.mark.parametrize("F,T,C,R,first,last,see_all,dtype,d", [
@@ -173,9 +155,7 @@ def test_batch_stride_beyond_2_31_elements():
     torch.cuda.synchronize()
     refb = attention_backward(to_float64(x["q"]), to_float64(x["k"]), to_float64(x["v"]),
                               to_float64(gcpu))
-    for n, a, r in zip(("dQ", "dK", "dV"), (gq, gk, gv), refb):
-        err = float(np.max(np.abs(to_float64(a) - r)) / np.max(np.abs(r)))
-        assert err <= 2e-2, f"far batch stride backward: {n} normwise error {err:.3e}"
+    compare_bwd([to_float64(t) for t in (gq, gk, gv)], refb, "bf16", "far batch stride backward")
     del g, o, do, go, outs
     torch.cuda.empty_cache()
 

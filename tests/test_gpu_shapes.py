@@ -1,7 +1,7 @@
 """GPU parity for the general shapes of the op contract: Lq != Lkv
 (cross-attention) and d_qk != d_v, head dims 16, 32, 64, 128, 256 (bf16) and
 16, 32, 64 (float32), through attn_jvp_fwd_ex.  Every output row is compared
-with the float64 oracle; the tolerances are those of test_gpu_parity.
+with the float64 oracle under the bounds of tests/tolerances.py.
 """
 
 import numpy as np
@@ -11,23 +11,16 @@ import torch
 import attention_jvp_amd as aj
 from oracle import FrameWindow, attention_jvp
 from synth import Workload, make_inputs, to_float64
+from tolerances import compare_fwd, say
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"fp32": (1e-5, 1e-4), "bf16": (2e-2, 2e-2)}
 NAMES = ("q", "k", "v", "dq", "dk", "dv")
 BF16_DIMS = (16, 32, 64, 128, 256)
 FP32_DIMS = (16, 32, 64)
 
 
-def _say(*a):
-    print(*a, flush=True)
-
-
-def _err(got, ref):
-    fin = np.isfinite(ref)
-    den = np.max(np.abs(ref[fin])) if fin.any() else 1.0
-    return float(np.max(np.abs(got[fin] - ref[fin])) / max(den, 1e-30)) if fin.any() else 0.0
+_say = say
 
 
 def _check(w, mask=None, scale=None, what=""):
@@ -40,13 +33,7 @@ def _check(w, mask=None, scale=None, what=""):
     vis = None if mask is None else FrameWindow(**{k: bool(v) if k.startswith("anchor") else v
                                                    for k, v in mask.items()})
     ref = attention_jvp(*(to_float64(x[n]) for n in NAMES), scale=scale, visible=vis)
-    tol_o, tol_do = TOL[w.dtype]
-    errs = {}
-    for n, a, r, t in zip(("O", "dO", "LSE", "dLSE"), gpu, ref, (tol_o, tol_do, tol_o, tol_do)):
-        assert np.array_equal(np.isfinite(a), np.isfinite(r)), f"{what}: {n} finiteness"
-        errs[n] = _err(a, r)
-        assert errs[n] <= t, f"{what}: {n} normwise error {errs[n]:.3e} > {t:.0e}"
-    _say(what, " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    compare_fwd(gpu, ref, w.dtype, what)
 
 
 @pytest.mark.parametrize("dqk", BF16_DIMS)
