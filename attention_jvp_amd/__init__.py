@@ -22,7 +22,10 @@ __all__ = [
     "attn_jvp_merge", "attn_jvp_splitkv_plan", "attn_jvp_fwd_splitkv", "exported_symbols",
     "fwd", "fwd_partial", "fwd_splitkv", "merge", "library_path", "load",
     "BwdLayout", "attn_jvp_bwd", "attn_jvp_bwd_check", "attn_jvp_bwd_visible_tiles", "bwd",
+    "attn_jvp_fwd_splitkv_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 ATTN_JVP_BF16 = 0
 ATTN_JVP_FP32 = 1
@@ -71,7 +74,7 @@ EXPORTS = ("attn_jvp_fwd", "attn_jvp_fwd_strided", "attn_jvp_fwd_ex", "attn_jvp_
            "attn_jvp_visible_tiles", "attn_jvp_fwd_partial", "attn_jvp_merge",
            "attn_jvp_splitkv_plan", "attn_jvp_fwd_splitkv", "attn_jvp_bwd",
            "attn_jvp_bwd_check", "attn_jvp_bwd_visible_tiles", "attn_jvp_status_string",
-           "attn_jvp_build_id")
+           "attn_jvp_build_id", "attn_jvp_fwd_splitkv_noalloc")
 
 
 def library_path():
@@ -126,6 +129,10 @@ def load():
                                                   ctypes.POINTER(Layout), ctypes.POINTER(Mask),
                                                   i32, vp, sz, vp]
     lib.attn_jvp_fwd_splitkv.restype = i32
+    lib.attn_jvp_fwd_splitkv_noalloc.argtypes = ptrs10 + [ctypes.POINTER(Shape), f32, i32,
+                                                          ctypes.POINTER(Layout),
+                                                          ctypes.POINTER(Mask), i32, vp]
+    lib.attn_jvp_fwd_splitkv_noalloc.restype = i32
     lib.attn_jvp_bwd.argtypes = [vp] * 10 + [ctypes.POINTER(Shape), f32, i32,
                                              ctypes.POINTER(BwdLayout), ctypes.POINTER(Mask), vp]
     lib.attn_jvp_bwd.restype = i32
@@ -225,6 +232,14 @@ def attn_jvp_fwd_splitkv(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, shape, scale, dt
     return load().attn_jvp_fwd_splitkv(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE,
                                        ctypes.byref(shape), scale, dtype, lay, _mask_ptr(mask),
                                        num_splits, workspace, workspace_bytes, stream)
+
+
+def attn_jvp_fwd_splitkv_noalloc(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, shape, scale, dtype,
+                                 layout, mask, num_splits, stream=None):
+    lay = None if layout is None else ctypes.byref(layout)
+    return load().attn_jvp_fwd_splitkv_noalloc(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE,
+                                               ctypes.byref(shape), scale, dtype, lay,
+                                               _mask_ptr(mask), num_splits, stream)
 
 
 def attn_jvp_bwd(Q, K, V, O, gO, LSE, gQ, gK, gV, delta, shape, scale, dtype, layout=None,

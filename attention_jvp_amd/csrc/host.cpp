@@ -533,6 +533,8 @@ const char *attn_jvp_status_string(int status) {
              "pointer or stride, or outputs overlapping inputs)";
     case ATTN_JVP_EMASK: return "inconsistent mask descriptor";
     case ATTN_JVP_EHIP: return "HIP runtime error at launch";
+    case ATTN_JVP_ENOSCRATCH:
+      return "the split partials exceed the static scratch of the allocation-free entry point";
     default: return "unknown status";
   }
 }

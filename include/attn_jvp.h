@@ -73,7 +73,9 @@ typedef enum {
   ATTN_JVP_ESTRIDE = -3,     /* tangent strides differ from the primal's, a
                                 misaligned pointer or stride, or overlap    */
   ATTN_JVP_EMASK = -4,       /* inconsistent mask descriptor                */
-  ATTN_JVP_EHIP = -5         /* the HIP runtime reported an error at launch */
+  ATTN_JVP_EHIP = -5,        /* the HIP runtime reported an error at launch */
+  ATTN_JVP_ENOSCRATCH = -6   /* the call's split partials exceed the static
+                                scratch of attn_jvp_fwd_splitkv_noalloc     */
 } attn_jvp_status;
 
 enum { ATTN_JVP_MASK_NONE = 0, ATTN_JVP_MASK_FRAME_WINDOW = 1 };
@@ -198,6 +200,35 @@ int attn_jvp_fwd_splitkv(const void *Q, const void *K, const void *V,
                          const attn_jvp_layout *layout,
                          const attn_jvp_mask *mask, int num_splits,
                          void *workspace, size_t workspace_bytes, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * attn_jvp_fwd_splitkv with the float32 partials in a static device buffer of
+ * the library instead of a caller workspace.  The caller still passes every
+ * input and output.  Same arguments, rules and results as
+ * attn_jvp_fwd_splitkv without workspace/workspace_bytes; no allocating call
+ * is made.
+ *  - The buffer holds ATTN_JVP_NOALLOC_SCRATCH_BYTES (64 MiB) on each GPU the
+ *    library runs on, until the process ends.  A call whose plan needs more
+ *    (attn_jvp_splitkv_plan's workspace_bytes) returns ATTN_JVP_ENOSCRATCH
+ *    when num_splits is given; with num_splits = 0 the plan takes the most
+ *    splits that fit (one split needs no buffer).
+ *  - Every call on a GPU shares that GPU's buffer: calls that overlap in
+ *    time on one GPU (two streams, or two host threads) race and give wrong
+ *    results; serialise them.  The buffer keeps the last call's partials;
+ *    nothing in it needs to start at zero (every split writes all its rows).
+ *  - The stream must belong to the current device (else ATTN_JVP_EINVAL).
+ *    The first call on a device looks up that device's buffer address once
+ *    (hipGetSymbolAddress); make that first call outside graph capture.
+ * Returns a status; nothing is launched unless it is ATTN_JVP_OK. */
+#define ATTN_JVP_NOALLOC_SCRATCH_BYTES (64u << 20)
+int attn_jvp_fwd_splitkv_noalloc(const void *Q, const void *K, const void *V,
+                                 const void *dQ, const void *dK, const void *dV,
+                                 void *O, void *dO, float *LSE, float *dLSE,
+                                 const attn_jvp_shape *shape, float scale,
+                                 int dtype, const attn_jvp_layout *layout,
+                                 const attn_jvp_mask *mask, int num_splits,
+                                 void *stream);
 
 /* ---- Primal backward --------------------------------------------------
  * Gradients of a loss L through O = softmax(s Q K^T) V, from the row

@@ -172,9 +172,20 @@ def test_splitkv_errors_launch_nothing():
     ns, need = aj.attn_jvp_splitkv_plan(shape, aj.ATTN_JVP_BF16, None, 4)
     assert ns == 4 and need > 0
     small = torch.empty(need - 256, device="cuda", dtype=torch.uint8)
-    with pytest.raises(aj.AttnJvpError) as e:
+    # the binding refuses a short workspace before the call ...
+    with pytest.raises(ValueError):
         aj.fwd_splitkv(*g, num_splits=4, workspace=small)
-    assert e.value.status == -1
+    # ... and so does the C entry point
+    o = torch.empty((1, 1, 64, 128), device="cuda", dtype=torch.bfloat16)
+    do = torch.empty_like(o)
+    lse = torch.empty((1, 1, 64), device="cuda")
+    dlse = torch.empty_like(lse)
+    lay = aj.layout_of(*g, o, do)
+    st = aj.attn_jvp_fwd_splitkv(*(t.data_ptr() for t in g), o.data_ptr(), do.data_ptr(),
+                                 lse.data_ptr(), dlse.data_ptr(), shape, 0.0, aj.ATTN_JVP_BF16,
+                                 lay, None, 4, small.data_ptr(), need - 256,
+                                 torch.cuda.current_stream().cuda_stream)
+    assert st == -1
     # a workspace that overlaps an input
     with pytest.raises(aj.AttnJvpError) as e:
         big = torch.empty(need + 2 * 2000 * 128 * 2, device="cuda", dtype=torch.uint8)
