@@ -2,12 +2,20 @@
 #pragma once
 
 #include "dispatch.h"
+#if ATTN_JVP_ROWS32_D128 || ATTN_JVP_ROWS32_D64
+#include "kernel32.h"
+#endif
 
 namespace attn_jvp {
 
 // A frame-window mask is built for d_qk == d_v only.
 template <typename T, int DQK, int DV>
 hipError_t launch_pair(const Params &p, bool masked, hipStream_t s) {
+#if ATTN_JVP_ROWS32_D128 || ATTN_JVP_ROWS32_D64
+  if constexpr (use_rows32((int)sizeof(T), DQK, DV)) {
+    return masked ? launch_instance32<DQK, true>(p, s) : launch_instance32<DQK, false>(p, s);
+  }
+#endif
   if (masked) {
     if constexpr (DQK == DV) return launch_instance<T, DQK, DV, true>(p, s);
     else return hipErrorInvalidValue;

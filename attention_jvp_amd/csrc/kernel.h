@@ -77,7 +77,7 @@ struct Cfg {
   static constexpr int ES = (int)sizeof(T);
   static constexpr int RBK = DQK * ES;   // bytes per K / dK row
   static constexpr int RBV = DV * ES;    // bytes per V / dV row
-  static constexpr FwdGeom G = fwd_geom(ES, DQK, DV);
+  static constexpr FwdGeom G = fwd16_geom(ES, DQK, DV);
   static constexpr int kWaves = G.waves;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kBlockM = G.block_m;
@@ -194,15 +194,43 @@ __device__ inline int bswz(int r) {
   else return kswz<RB>(r);
 }
 
+// Rules of the 32-query-row kernel (kernel32.h), whose operand-row reads
+// cover 32 consecutive rows (a 16-lane pass reads rows r mod 32 in
+// {0-3, 12-15, 20-23, 24-27} or {4-11, 16-19, 28-31}, all at one chunk) and
+// whose transposing reads cover 4 consecutive rows x 64 bytes per pass:
+//  * k32swz(r): 16 distinct slots over each pass's rows (r mod 16 for
+//    256-byte rows; for 128-byte rows two rows share a bank sweep, so
+//    (r mod 2, slot) must differ: slot (r / 2) mod 8);
+//  * v32swz(r): the four rows' 64-byte runs on distinct quarters of the
+//    bank sweep (4 (r mod 4) for 256-byte rows, 4 ((r / 2) mod 2) for
+//    128-byte rows).
+template <int RB>
+__device__ inline int k32swz(int r) {
+  static_assert(RB == 256 || RB == 128, "32-row rules are built for d = 128 and 64");
+  if constexpr (RB == 256) return r % 16;
+  else return (r >> 1) % 8;
+}
+
+template <int RB>
+__device__ inline int v32swz(int r) {
+  static_assert(RB == 256 || RB == 128, "32-row rules are built for d = 128 and 64");
+  if constexpr (RB == 256) return 4 * (r % 4);
+  else return 4 * ((r >> 1) & 1);
+}
+
 // swizzle kinds (template argument KS below)
 constexpr int kSwzV = 0;
 constexpr int kSwzK = 1;
 constexpr int kSwzB = 2;
+constexpr int kSwzK32 = 3;
+constexpr int kSwzV32 = 4;
 
 template <int RB, int KS>
 __device__ inline int swz(int r) {
   if constexpr (KS == kSwzK) return kswz<RB>(r);
   else if constexpr (KS == kSwzV) return vswz<RB>(r);
+  else if constexpr (KS == kSwzK32) return k32swz<RB>(r);
+  else if constexpr (KS == kSwzV32) return v32swz<RB>(r);
   else return bswz<RB>(r);
 }
 

@@ -32,15 +32,40 @@ namespace attn_jvp {
 // ---------------------------------------------------------------------------
 struct FwdGeom {
   int waves, block_m, block_n, lds;
+  bool rows32;   // the 32-query-row kernel (kernel32.h)
 };
 
-constexpr FwdGeom fwd_geom(int es, int dqk, int dv) {
+constexpr FwdGeom fwd16_geom(int es, int dqk, int dv) {
   const int resident = (es == 2 ? dqk / 4 : dqk / 2) + 3 * dv / 4;
   const int waves = (es == 2 && dqk == 64 && dv == 64) ? 12
                                                        : (resident <= (es == 2 ? 128 : 64) ? 8 : 4);
   const int row_bytes = (dqk + dv) * es;
   const int bn = 4 * 64 * row_bytes <= 128 * 1024 ? 64 : 32;
-  return FwdGeom{waves, 16 * waves, bn, 4 * bn * row_bytes};
+  return FwdGeom{waves, 16 * waves, bn, 4 * bn * row_bytes, false};
+}
+
+// The 32-query-row kernel for bfloat16 d_qk = d_v, built only when
+// ATTN_JVP_ROWS32_D128 or _D64 is defined to 1: four waves of 32 rows (one
+// per SIMD), 32-key steps, four LDS stages of K, dK, V, dV, 32x32x16 MFMAs.
+// Its resident registers (Q, dQ, O, A, B: about 256 per lane at d = 128)
+// allow one wave per SIMD, so the softmax work of a step cannot hide behind
+// another wave's MFMAs; measured at 1.18 ms against 0.92 ms for the 16-row
+// kernel on 2 x 24 heads x 4096 tokens at d = 128, it stays off by default.
+#ifndef ATTN_JVP_ROWS32_D128
+#define ATTN_JVP_ROWS32_D128 0
+#endif
+#ifndef ATTN_JVP_ROWS32_D64
+#define ATTN_JVP_ROWS32_D64 0
+#endif
+
+constexpr bool use_rows32(int es, int dqk, int dv) {
+  return es == 2 && dqk == dv &&
+         ((dqk == 128 && ATTN_JVP_ROWS32_D128) || (dqk == 64 && ATTN_JVP_ROWS32_D64));
+}
+
+constexpr FwdGeom fwd_geom(int es, int dqk, int dv) {
+  return use_rows32(es, dqk, dv) ? FwdGeom{4, 128, 32, 4 * 4 * 32 * dqk * es, true}
+                                 : fwd16_geom(es, dqk, dv);
 }
 
 // Head dims with a compiled forward instance: d_qk, d_v in {16, 32, 64, 128,

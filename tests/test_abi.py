@@ -120,13 +120,13 @@ def test_bad_mask(mask):
 
 
 def test_status_strings():
-    for s in (0, -1, -2, -3, -4, -5):
+    for s in (0, -1, -2, -3, -4, -5, -6):
         assert aj.attn_jvp_status_string(s)
     assert aj.attn_jvp_status_string(-99) == "unknown status"
 
 
 def test_tile_shape():
-    assert aj.attn_jvp_tile_shape(0, 128) == (128, 64)
+    assert aj.attn_jvp_tile_shape(0, 128) == (128, 64)    # bf16 d = 128: eight waves
     assert aj.attn_jvp_tile_shape(0, 64) == (192, 64)     # bf16 d = 64: twelve waves
     assert aj.attn_jvp_tile_shape(1, 64) == (64, 64)     # float32: four waves
     with pytest.raises(aj.AttnJvpError):
@@ -137,6 +137,7 @@ def test_tile_shape_unequal_head_dims():
     # eight waves x 16 rows while the resident registers fit two waves per
     # SIMD, else four; 64-key tiles while two LDS stages fit in 128 KiB
     assert aj.attn_jvp_tile_shape_ex(0, 128, 128) == (128, 64)
+    assert aj.attn_jvp_tile_shape_ex(0, 128, 64) == (128, 64)
     assert aj.attn_jvp_tile_shape_ex(0, 256, 256) == (64, 32)
     assert aj.attn_jvp_tile_shape_ex(0, 256, 64) == (128, 32)
     assert aj.attn_jvp_tile_shape_ex(0, 64, 256) == (64, 32)
@@ -263,7 +264,8 @@ def test_dense_scheduler_visits_every_tile():
 def test_long_video_visited_fraction():
     mask = dict(frames=42, tokens_per_frame=1560, chunk_frames=5, radius_chunks=1)
     got = aj.attn_jvp_visible_tiles(65520, 0, 128, mask)
-    total = len(got) * ((65520 + 63) // 64)
+    _, bn = aj.attn_jvp_tile_shape(0, 128)
+    total = len(got) * ((65520 + bn - 1) // bn)
     assert 0.36 < sum(got) / total < 0.38
 
 
