@@ -93,6 +93,32 @@ def test_large_logits_bf16():
     _full_check(w, scale=4.0, lse_abs=1e-3)
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 16), ("bf16", 32), ("bf16", 64), ("bf16", 128),
+                                     ("bf16", 256), ("fp32", 16), ("fp32", 64)])
+@pytest.mark.parametrize("rising", [True, False])
+def test_logits_ramp_along_keys(dtype, d, rising):
+    # q_0 = 4 and k_0 a ramp over the keys from -8 to 8 (or back): the row
+    # maxima grow through the whole walk (the reference moves every few
+    # tiles) or peak in the first tile (it never moves again); 700 keys are
+    # several tiles and a ragged tail.  Scores reach |S| ~ 60, where their
+    # float32 rounding (relative 2^-24 of each product sum) moves P by up to
+    # ~1e-5: float32 O is held to the contract there, not the unit-score
+    # ceiling
+    N = 700
+    _say(f"ramp {dtype} d{d} {'rising' if rising else 'falling'}")
+    w = Workload("ramp", 1, 2, N, d, dtype, 40 + d, tangent_scale=0.1)
+    x = make_inputs(w)
+    ramp = torch.linspace(-8.0, 8.0, N) if rising else torch.linspace(8.0, -8.0, N)
+    x["q"][..., 0] = 4.0
+    x["k"][..., 0] = ramp.to(x["k"].dtype)
+    out = _run(x, scale=1.0)
+    gpu = [to_float64(t) for t in out]
+    ref = attention_jvp(*(to_float64(x[n]) for n in NAMES), scale=1.0)
+    _compare(gpu, ref, dtype, f"ramp {dtype} d{d} rising={rising}",
+             lse_abs=1e-3 if dtype == "bf16" else 1e-4,
+             ceiling={"O": 1e-5} if dtype == "fp32" else None)
+
+
 @pytest.mark.parametrize("F,T,C,R,first,last,see_all,dtype,d", [
     (7, 37, 2, 1, 1, 1, 0, "bf16", 128),
     (9, 64, 3, 0, 1, 0, 0, "bf16", 64),
