@@ -22,7 +22,7 @@ __all__ = [
     "attn_jvp_merge", "attn_jvp_splitkv_plan", "attn_jvp_fwd_splitkv", "exported_symbols",
     "fwd", "fwd_partial", "fwd_splitkv", "merge", "library_path", "load",
     "BwdLayout", "attn_jvp_bwd", "attn_jvp_bwd_check", "attn_jvp_bwd_visible_tiles", "bwd",
-    "attn_jvp_fwd_splitkv_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "attn_jvp_fwd_splitkv_noalloc", "NOALLOC_SCRATCH_BYTES", "attn_jvp_fwd_geometry",
 ]
 
 NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -74,7 +74,7 @@ EXPORTS = ("attn_jvp_fwd", "attn_jvp_fwd_strided", "attn_jvp_fwd_ex", "attn_jvp_
            "attn_jvp_visible_tiles", "attn_jvp_fwd_partial", "attn_jvp_merge",
            "attn_jvp_splitkv_plan", "attn_jvp_fwd_splitkv", "attn_jvp_bwd",
            "attn_jvp_bwd_check", "attn_jvp_bwd_visible_tiles", "attn_jvp_status_string",
-           "attn_jvp_build_id", "attn_jvp_fwd_splitkv_noalloc")
+           "attn_jvp_build_id", "attn_jvp_fwd_splitkv_noalloc", "attn_jvp_fwd_geometry")
 
 
 def library_path():
@@ -116,6 +116,9 @@ def load():
     lib.attn_jvp_check_ex.restype = i32
     lib.attn_jvp_tile_shape_ex.argtypes = [i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.attn_jvp_tile_shape_ex.restype = i32
+    lib.attn_jvp_fwd_geometry.argtypes = [ctypes.POINTER(Shape), i32, ctypes.POINTER(Mask),
+                                          ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.attn_jvp_fwd_geometry.restype = i32
     lib.attn_jvp_fwd_partial.argtypes = ptrs10 + [ctypes.POINTER(Shape), f32, i32,
                                                   ctypes.POINTER(Layout), vp]
     lib.attn_jvp_fwd_partial.restype = i32
@@ -261,6 +264,17 @@ def attn_jvp_tile_shape_ex(dtype, d_qk, d_v):
     st = load().attn_jvp_tile_shape_ex(dtype, d_qk, d_v, ctypes.byref(bm), ctypes.byref(bn))
     if st != 0:
         raise AttnJvpError(st, "attn_jvp_tile_shape_ex")
+    return bm.value, bn.value
+
+
+def attn_jvp_fwd_geometry(B, H, Lq, Lkv, d_qk, d_v, dtype, mask=None):
+    """(block_m, block_n) that attn_jvp_fwd_ex launches for this call."""
+    bm, bn = ctypes.c_int(), ctypes.c_int()
+    shape = Shape(B, H, Lq, Lkv, d_qk, d_v)
+    st = load().attn_jvp_fwd_geometry(ctypes.byref(shape), dtype, _mask_ptr(mask),
+                                      ctypes.byref(bm), ctypes.byref(bn))
+    if st != 0:
+        raise AttnJvpError(st, "attn_jvp_fwd_geometry")
     return bm.value, bn.value
 
 

@@ -114,8 +114,8 @@ int attn_jvp_fwd_ex(const void *Q, const void *K, const void *V, const void *dQ,
   const attn_jvp_layout L = layout ? *layout : contiguous(*shape);
   const int st = check_args(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, shape, dtype, &L, mask);
   if (st != ATTN_JVP_OK) return st;
-  const Params p = make_params(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, *shape, scale, dtype, L,
-                               mask);
+  Params p = make_params(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, *shape, scale, dtype, L, mask);
+  if (launch_small(*shape, dtype, mask)) set_small(&p, dtype, *shape);
   return status_of(dispatch(p, dtype, shape->head_dim_qk, shape->head_dim_v, mask_on(mask),
                             (hipStream_t)stream));
 }

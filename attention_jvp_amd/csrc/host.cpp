@@ -106,6 +106,22 @@ bool shape_for(int dtype, int dqk, int dv, FwdGeom *out) {
   return true;
 }
 
+bool launch_small(const attn_jvp_shape &s, int dtype, const attn_jvp_mask *mask) {
+  if (!dtype_ok(dtype)) return false;
+  const int es = esize_of(dtype), dqk = s.head_dim_qk, dv = s.head_dim_v;
+  if (!fwd_pick_small(es, dqk, dv, (int64_t)s.batch * s.heads, s.seqlen_q, mask_on(mask), 1))
+    return false;
+  const FwdGeom g = fwd16_geom_small(es, dqk, dv);
+  return grid_fits((int64_t)s.batch * s.heads * ((s.seqlen_q + g.block_m - 1) / g.block_m),
+                   64 * g.waves);
+}
+
+void set_small(Params *p, int dtype, const attn_jvp_shape &s) {
+  const FwdGeom g = fwd16_geom_small(esize_of(dtype), s.head_dim_qk, s.head_dim_v);
+  p->small = 1;
+  p->nqb = (p->Nq + g.block_m - 1) / g.block_m;
+}
+
 attn_jvp_layout contiguous(const attn_jvp_shape &s) {
   attn_jvp_layout L;
   const int64_t nq = s.seqlen_q, nkv = s.seqlen_kv, dqk = s.head_dim_qk, dv = s.head_dim_v;
@@ -486,6 +502,20 @@ int attn_jvp_tile_shape_ex(int dtype, int d_qk, int d_v, int *block_m, int *bloc
 
 int attn_jvp_tile_shape(int dtype, int d, int *block_m, int *block_n) {
   return attn_jvp_tile_shape_ex(dtype, d, d, block_m, block_n);
+}
+
+int attn_jvp_fwd_geometry(const attn_jvp_shape *shape, int dtype, const attn_jvp_mask *mask,
+                          int *block_m, int *block_n) {
+  if (!shape || !block_m || !block_n) return ATTN_JVP_EINVAL;
+  const attn_jvp_shape &s = *shape;
+  if (s.batch <= 0 || s.heads <= 0 || s.seqlen_q <= 0 || s.seqlen_kv <= 0) return ATTN_JVP_EINVAL;
+  if (!dtype_ok(dtype)) return ATTN_JVP_EINVAL;
+  FwdGeom g;
+  if (!shape_for(dtype, s.head_dim_qk, s.head_dim_v, &g)) return ATTN_JVP_EUNSUPPORTED;
+  if (launch_small(s, dtype, mask)) g = fwd16_geom_small(esize_of(dtype), s.head_dim_qk, s.head_dim_v);
+  *block_m = g.block_m;
+  *block_n = g.block_n;
+  return ATTN_JVP_OK;
 }
 
 int attn_jvp_visible_tiles(int N, int dtype, int d, const attn_jvp_mask *mask,

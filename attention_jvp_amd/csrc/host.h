@@ -24,6 +24,11 @@ MaskDev to_dev(const attn_jvp_mask *mask);
 // built.
 bool shape_for(int dtype, int dqk, int dv, FwdGeom *out);
 
+// Does an unsplit forward launch of this call take the small geometry
+// (fwd16_geom_small)?  set_small switches a launch's parameters to it.
+bool launch_small(const attn_jvp_shape &s, int dtype, const attn_jvp_mask *mask);
+void set_small(Params *p, int dtype, const attn_jvp_shape &s);
+
 attn_jvp_layout contiguous(const attn_jvp_shape &s);
 attn_jvp_bwd_layout contiguous_bwd(const attn_jvp_shape &s);
 attn_jvp_shape square(int B, int H, int N, int d);

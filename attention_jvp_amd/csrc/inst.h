@@ -20,6 +20,10 @@ hipError_t launch_pair(const Params &p, bool masked, hipStream_t s) {
     if constexpr (DQK == DV) return launch_instance<T, DQK, DV, true>(p, s);
     else return hipErrorInvalidValue;
   }
+  if constexpr (fwd_has_small((int)sizeof(T), DQK, DV)) {
+    if (p.small) return launch_instance<T, DQK, DV, false, true>(p, s);
+  }
+  if (p.small) return hipErrorInvalidValue;
   return launch_instance<T, DQK, DV, false>(p, s);
 }
 

@@ -72,12 +72,12 @@ constexpr int kStepKeys = 32;   // keys per softmax step
 // ---------------------------------------------------------------------------
 // Launch shape of one (dtype, d_qk, d_v) instance.
 // ---------------------------------------------------------------------------
-template <typename T, int DQK, int DV>
+template <typename T, int DQK, int DV, bool SMALL = false>
 struct Cfg {
   static constexpr int ES = (int)sizeof(T);
   static constexpr int RBK = DQK * ES;   // bytes per K / dK row
   static constexpr int RBV = DV * ES;    // bytes per V / dV row
-  static constexpr FwdGeom G = fwd16_geom(ES, DQK, DV);
+  static constexpr FwdGeom G = SMALL ? fwd16_geom_small(ES, DQK, DV) : fwd16_geom(ES, DQK, DV);
   static constexpr int kWaves = G.waves;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kBlockM = G.block_m;
@@ -397,9 +397,11 @@ __device__ inline void wait_vmem() {
 // more with it (2 % slower): both keep the plain row maximum.
 constexpr float kRescaleThreshold = 8.0f;
 
-template <typename T, int DQK, int DV, bool MASKED>
-__global__ __launch_bounds__((Cfg<T, DQK, DV>::kThreads), 1) void attn_jvp_kernel(Params p) {
-  using C = Cfg<T, DQK, DV>;
+// The small geometry runs three workgroups per CU (at most 168 registers).
+template <typename T, int DQK, int DV, bool MASKED, bool SMALL = false>
+__global__ __launch_bounds__((Cfg<T, DQK, DV, SMALL>::kThreads), (SMALL ? 3 : 1))
+void attn_jvp_kernel(Params p) {
+  using C = Cfg<T, DQK, DV, SMALL>;
   using EK = ElemK<T, DQK>;
   using EV = ElemV<T>;
   using FragK = typename EK::Frag;
@@ -641,7 +643,7 @@ __global__ __launch_bounds__((Cfg<T, DQK, DV>::kThreads), 1) void attn_jvp_kerne
   // ---- running max (log2 domain) and lazy rescale of the accumulators ----
   // IEEE maximum (NaN-propagating): v_maximum3_f32, no canonicalisation
   constexpr bool kOverlap = BF16 && NSTEP == 2 && DQK + DV >= 256;
-  constexpr bool kLaneCheck = !kOverlap && W >= 8;
+  constexpr bool kLaneCheck = !kOverlap && (W >= 8 || SMALL);   // two or more waves per SIMD
   auto update_max = [&](const f32x4 (&sacc)[2]) __attribute__((always_inline)) {
     // eight scores in a tree of three-input maxima
     auto mx3 = [](float a, float b, float c) __attribute__((always_inline)) {
@@ -897,12 +899,12 @@ __global__ __launch_bounds__((Cfg<T, DQK, DV>::kThreads), 1) void attn_jvp_kerne
 }
 
 // Launch one instance: grid = B * H * ceil(Nq / block_m) * nsplit workgroups.
-template <typename T, int DQK, int DV, bool MASKED>
+template <typename T, int DQK, int DV, bool MASKED, bool SMALL = false>
 hipError_t launch_instance(const Params &p, hipStream_t stream) {
-  using C = Cfg<T, DQK, DV>;
+  using C = Cfg<T, DQK, DV, SMALL>;
   const int grid = p.B * p.H * p.nqb * p.nsplit;
-  hipLaunchKernelGGL((attn_jvp_kernel<T, DQK, DV, MASKED>), dim3(grid), dim3(C::kThreads), 0,
-                     stream, p);
+  hipLaunchKernelGGL((attn_jvp_kernel<T, DQK, DV, MASKED, SMALL>), dim3(grid), dim3(C::kThreads),
+                     0, stream, p);
   return hipGetLastError();
 }
 

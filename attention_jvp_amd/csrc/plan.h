@@ -44,6 +44,36 @@ constexpr FwdGeom fwd16_geom(int es, int dqk, int dv) {
   return FwdGeom{waves, 16 * waves, bn, 4 * bn * row_bytes, false};
 }
 
+// A second geometry of bfloat16 d_qk = d_v = 64 for grids that the twelve-
+// wave blocks fill badly: four waves (64 query rows) and 32-key tiles, so
+// that three workgroups share a CU (the same three waves per SIMD, 32 KiB of
+// LDS each) and the grid comes in thirds of the 192-row blocks.  Its waves
+// run a little slower (each workgroup copies every key tile for 64 rows, and
+// waits at a barrier every 32 keys): 0.4-4.5 % where both grids end in a
+// full round of the chip.  fwd_pick_small takes it when the twelve-wave
+// grid's round count exceeds the small grid's by more than 10 %: measured
+// 2 x 24 x 4096 (4.1 rounds of 192-row blocks against 4 of 64-row blocks)
+// 9.6 % faster, 8 x 24 x 1024 11 %, 1 x 24 x 16384 (8.1 against 8) 3.8 %;
+// the text-to-image 4 x 16 x 4352 (6 rounds either way) keeps the twelve
+// waves.  Never with a mask or key splits (their tile lists follow the
+// default geometry).
+constexpr bool fwd_has_small(int es, int dqk, int dv) {
+  return es == 2 && dqk == 64 && dv == 64;
+}
+
+constexpr FwdGeom fwd16_geom_small(int es, int dqk, int dv) {
+  return FwdGeom{4, 64, 32, 4 * 32 * (dqk + dv) * es, false};
+}
+
+// bh = batch x heads; cus = compute units (256 on MI355X).
+inline bool fwd_pick_small(int es, int dqk, int dv, int64_t bh, int64_t nq, bool masked,
+                           int nsplit, int cus = 256) {
+  if (!fwd_has_small(es, dqk, dv) || masked || nsplit != 1) return false;
+  const int64_t wg12 = bh * ((nq + 191) / 192), wg4 = bh * ((nq + 63) / 64);
+  const int64_t r12 = (wg12 + cus - 1) / cus, r4 = (wg4 + 3 * cus - 1) / (3 * cus);
+  return (double)r4 * 1.1 < (double)r12;
+}
+
 // The 32-query-row kernel for bfloat16 d_qk = d_v, built only when
 // ATTN_JVP_ROWS32_D128 or _D64 is defined to 1: four waves of 32 rows (one
 // per SIMD), 32-key steps, four LDS stages of K, dK, V, dV, 32x32x16 MFMAs.
@@ -238,6 +268,7 @@ struct Params {
   int nqb;                              // query blocks per (b, h)
   int nsplit;                           // key splits per query block (1: none)
   int partial;                          // 1: outputs are float32 partials
+  int small;                            // 1: the small geometry (fwd16_geom_small)
   float scale, scale_log2;
   MaskDev mask;
 };

@@ -300,11 +300,24 @@ int attn_jvp_check(const void *Q, const void *K, const void *V,
                    const attn_jvp_layout *layout, const attn_jvp_mask *mask);
 
 /* Host-only: the query-block rows (block_m) and key-tile length (block_n) the
- * library uses for (dtype, d_qk = d_v = d); returns a status. */
+ * library uses for (dtype, d_qk = d_v = d); returns a status.  This is the
+ * geometry of every masked, key-split and partial launch, and of most
+ * others (see attn_jvp_fwd_geometry). */
 int attn_jvp_tile_shape(int dtype, int d, int *block_m, int *block_n);
 
 /* The same for unequal head dims (dtype, d_qk, d_v). */
 int attn_jvp_tile_shape_ex(int dtype, int d_qk, int d_v, int *block_m, int *block_n);
+
+/* Host-only: the geometry (query-block rows, key-tile length) that
+ * attn_jvp_fwd_ex launches for this call.  It is attn_jvp_tile_shape_ex's,
+ * except for unmasked bfloat16 d_qk = d_v = 64 calls whose grid of 192-row
+ * blocks would leave much of its last round of the chip idle: those take
+ * 64-row blocks and 32-key tiles (three workgroups per compute unit).  The
+ * choice depends on batch x heads and seqlen_q only.  Returns
+ * ATTN_JVP_EINVAL for a NULL argument or a non-positive size,
+ * ATTN_JVP_EUNSUPPORTED for head dims that are not built. */
+int attn_jvp_fwd_geometry(const attn_jvp_shape *shape, int dtype, const attn_jvp_mask *mask,
+                          int *block_m, int *block_n);
 
 /* Host-only: the key tiles the scheduler visits for each query block of an
  * N-token sequence under `mask` (NULL = dense) with the tile shape of

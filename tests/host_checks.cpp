@@ -233,6 +233,43 @@ static void check_validation() {
   const FwdGeom g = fwd_geom(2, 128, 128);
   CHECK(!grid_fits(((int64_t)1 << 32) / (64 * g.waves) + 1, 64 * g.waves), "grid limit");
   CHECK(grid_fits(((int64_t)1 << 32) / (64 * g.waves) - 1, 64 * g.waves), "grid limit");
+  // the small geometry: only unmasked bfloat16 d_qk = d_v = 64, its grid
+  // within the launch limits, and the query reports what the launch takes
+  {
+    const attn_jvp_mask fw = {ATTN_JVP_MASK_FRAME_WINDOW, 4, 64, 2, 1, 1, 1, 0};
+    uint64_t y = 0x243f6a8885a308d3ull;
+    const int dims[5] = {16, 32, 64, 128, 256};
+    int taken = 0;
+    for (int i = 0; i < 20000; ++i) {
+      y ^= y << 13;
+      y ^= y >> 7;
+      y ^= y << 17;
+      const int d = dims[y % 5], dtype = (int)((y >> 8) % 2);
+      const bool masked = (y >> 60) & 1;   // the window holds 256 tokens
+      const int bh = 1 + (int)((y >> 16) % 4096);
+      const int nq = masked ? 256 : 1 + (int)((y >> 32) % 70000);
+      const attn_jvp_shape sh = {1, bh, nq, nq, d, d};
+      const bool sm = launch_small(sh, dtype, masked ? &fw : nullptr);
+      if (sm) {
+        ++taken;
+        CHECK(dtype == ATTN_JVP_BF16 && d == 64 && !masked, "small geometry for dtype %d d %d", dtype, d);
+        const FwdGeom gs = fwd16_geom_small(2, 64, 64);
+        CHECK(grid_fits((int64_t)bh * ((nq + gs.block_m - 1) / gs.block_m), 64 * gs.waves),
+              "small grid beyond the launch limits");
+      }
+      int bm = 0, bn = 0;
+      const int gst = attn_jvp_fwd_geometry(&sh, dtype, masked ? &fw : nullptr, &bm, &bn);
+      if (fwd_built(dtype == ATTN_JVP_BF16 ? 2 : 4, d, d)) {
+        const FwdGeom gd = fwd_geom(dtype == ATTN_JVP_BF16 ? 2 : 4, d, d);
+        const FwdGeom ge = sm ? fwd16_geom_small(2, 64, 64) : gd;
+        CHECK(gst == ATTN_JVP_OK && bm == ge.block_m && bn == ge.block_n,
+              "fwd_geometry %d: (%d, %d)", gst, bm, bn);
+      } else {
+        CHECK(gst == ATTN_JVP_EUNSUPPORTED, "fwd_geometry of an unbuilt dim: %d", gst);
+      }
+    }
+    CHECK(taken > 0, "the small geometry never taken");
+  }
   // pseudo-random calls: every one returns a status, and OK only for calls
   // that satisfy the documented rules this loop can state
   uint64_t x = 0x9e3779b97f4a7c15ull;

@@ -133,6 +133,30 @@ def test_tile_shape():
         aj.attn_jvp_tile_shape(1, 128)
 
 
+def test_fwd_geometry_by_grid():
+    # bf16 d = 64 without a mask: 64-row blocks and 32-key tiles where the
+    # 192-row grid would end in a mostly idle round of the 256 CUs
+    g = aj.attn_jvp_fwd_geometry
+    assert g(2, 24, 4096, 4096, 64, 64, 0) == (64, 32)     # 4.1 rounds of 192 rows
+    assert g(8, 24, 1024, 1024, 64, 64, 0) == (64, 32)
+    assert g(8, 6, 1000, 1000, 64, 64, 0) == (64, 32)      # 2 rounds against 1
+    assert g(4, 16, 4352, 4352, 64, 64, 0) == (192, 64)    # 5.75 rounds
+    assert g(1, 16, 8192, 8192, 64, 64, 0) == (192, 64)
+    assert g(1, 24, 16384, 16384, 64, 64, 0) == (64, 32)    # 8.1 rounds against 8
+    assert g(1, 2, 300, 300, 64, 64, 0) == (192, 64)       # below one round either way
+    # the default geometry everywhere else: masks, other head dims, float32
+    mask = dict(frames=32, tokens_per_frame=128, chunk_frames=2, radius_chunks=1)
+    assert g(2, 24, 4096, 4096, 64, 64, 0, mask) == aj.attn_jvp_tile_shape(0, 64)
+    assert g(2, 24, 4096, 4096, 128, 128, 0) == aj.attn_jvp_tile_shape(0, 128)
+    assert g(2, 24, 4096, 4096, 64, 128, 0) == aj.attn_jvp_tile_shape_ex(0, 64, 128)
+    assert g(2, 24, 4096, 4096, 64, 64, 1) == aj.attn_jvp_tile_shape(1, 64)
+    assert g(2, 24, 4096, 4096, 32, 32, 0) == aj.attn_jvp_tile_shape(0, 32)
+    for args in ((0, 24, 4096, 4096, 64, 64, 0), (2, 24, 4096, 0, 64, 64, 0),
+                 (2, 24, 4096, 4096, 48, 48, 0), (2, 24, 4096, 4096, 64, 64, 3)):
+        with pytest.raises(aj.AttnJvpError):
+            g(*args)
+
+
 def test_tile_shape_unequal_head_dims():
     # eight waves x 16 rows while the resident registers fit two waves per
     # SIMD, else four; 64-key tiles while two LDS stages fit in 128 KiB

@@ -135,6 +135,28 @@ def test_frame_window_mask_every_row(F, T, C, R, first, last, see_all, dtype, d)
     _full_check(w, mask=mask)
 
 
+@pytest.mark.parametrize("B,H,N", [(8, 6, 1000), (5, 8, 1200), (8, 6, 1024)])
+def test_small_geometry_every_row(B, H, N):
+    # bf16 d = 64 grids that take 64-row blocks and 32-key tiles (ragged
+    # last blocks for N = 1000 and 1200)
+    assert aj.attn_jvp_fwd_geometry(B, H, N, N, 64, 64, 0) == (64, 32)
+    _say(f"small geometry B{B} H{H} N{N}")
+    w = Workload("small-geometry", B, H, N, 64, "bf16", 500 + N, tangent_scale=0.1)
+    _full_check(w)
+
+
+def test_small_geometry_strided_views():
+    B, H, N, d = 8, 6, 1000, 64
+    assert aj.attn_jvp_fwd_geometry(B, H, N, N, d, d, 0) == (64, 32)
+    w = Workload("small-bshd", B, H, N, d, "bf16", 12, tangent_scale=0.1)
+    x = make_inputs(w)
+    g = {n: x[n].transpose(1, 2).contiguous().cuda().transpose(1, 2) for n in NAMES}
+    out = aj.fwd(*(g[n] for n in NAMES))
+    torch.cuda.synchronize()
+    ref = attention_jvp(*(to_float64(x[n]) for n in NAMES))
+    _compare([to_float64(t) for t in out], ref, "bf16", "small-geometry bshd")
+
+
 def test_strided_bshd_views():
     # tensors stored [B, N, H, d] and passed as [B, H, N, d] views
     B, H, N, d = 2, 3, 150, 128
