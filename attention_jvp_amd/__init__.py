@@ -416,9 +416,9 @@ def fwd(q, k, v, dq, dk, dv, scale=None, mask=None, out=None):
     """
     import torch
     dt, shape = check_qkv(q, k, v, dq, dk, dv)
+    _require_gpu(q, "q")
     o, do, lse, dlse = (_alloc_fwd_out(q, shape, q.dtype) if out is None
                         else check_fwd_out(out, q, shape))
-    _require_gpu(q, "q")
     lay = layout_of(q, k, v, dq, dk, dv, o, do)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     st = attn_jvp_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), dq.data_ptr(),
