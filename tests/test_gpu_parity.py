@@ -265,6 +265,34 @@ def test_nan_in_one_query_row_stays_in_that_row():
     assert torch.equal(bad.cpu(), expect.cpu())
 
 
+@pytest.mark.parametrize("tensor", ["k", "dk"])
+def test_nan_in_one_key_reaches_exactly_the_rows_that_see_it(tensor):
+    # under the frame window a key in a middle frame is seen by the queries
+    # of its chunk and the neighbouring ones only: those rows turn NaN, every
+    # other row (and every other head) matches the oracle, which hides the
+    # key from them before any arithmetic
+    F, T = 9, 37
+    mask = dict(frames=F, tokens_per_frame=T, chunk_frames=2, radius_chunks=1,
+                anchor_first=1, anchor_last=1, anchor_queries_see_all=0)
+    w = Workload("nan-key", 1, 2, F * T, 128, "bf16", 17, tangent_scale=0.1)
+    x = make_inputs(w)
+    x[tensor][0, 1, 4 * T + 5, 7] = float("nan")
+    gpu = [to_float64(t) for t in _run(x, mask=mask)]
+    vis = FrameWindow(**{k: bool(v) if k.startswith("anchor") else v for k, v in mask.items()})
+    ref = attention_jvp(*(to_float64(x[n]) for n in NAMES), visible=vis)
+
+    def nan_rows(out):
+        o, do, lse, dlse = out
+        return np.isnan(o).any(-1) | np.isnan(do).any(-1) | np.isnan(lse) | np.isnan(dlse)
+
+    bad, bad_ref = nan_rows(gpu), nan_rows(ref)
+    assert np.array_equal(bad, bad_ref)
+    assert bad_ref[0, 1].any() and not bad_ref[0, 1].all() and not bad_ref[0, 0].any()
+    keep = [np.where(bad_ref[..., None] if a.ndim == 4 else bad_ref, 0.0, a) for a in gpu]
+    keep_ref = [np.where(bad_ref[..., None] if a.ndim == 4 else bad_ref, 0.0, a) for a in ref]
+    _compare(keep, keep_ref, "bf16", f"NaN in one key of {tensor}")
+
+
 def test_zero_score_tangent_matches_output_with_dv_bitwise():
     # dQ = dK = 0: the tangent accumulator sums exactly the products the
     # output accumulator sums when V is replaced by dV
