@@ -113,6 +113,51 @@ def test_backward_rows_without_keys(dtype, d, Nq, Nkv):
     _say(f"bwd rows without keys {dtype} d{d}", " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
 
 
+@pytest.mark.parametrize("Nkv", [4096, 4001])
+def test_backward_image_dit_heads_sampled(Nkv):
+    # 2 x 24 heads x 4096 queries at d = 128: the dK/dV launch takes 128 keys
+    # per workgroup (at least 512 workgroups); 4001 keys leave a last block of
+    # 33 (one full wave of 32, one key in the next).  Every element of three
+    # heads against the oracle.
+    w = Workload("bwdI", 2, 24, 4096, 128, "bf16", 9320 + Nkv, rms_qk=True, tangent_scale=0.1,
+                 n_kv=Nkv)
+    x = make_inputs(w)
+    q, k, v = (x[n].cuda() for n in ("q", "k", "v"))
+    o, _, lse, _ = aj.fwd(*(x[n].cuda() for n in NAMES))
+    g_cpu = _grad_input(w, w.seed + 1)
+    gq, gk, gv, _ = aj.bwd(q, k, v, o, g_cpu.cuda(), lse)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (1, 23), (1, 7)):
+        sl = lambda t: to_float64(t[b:b + 1, h:h + 1])
+        ref = attention_backward(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(g_cpu))
+        what = f"bwd 2x24x4096x{Nkv} head ({b},{h})"
+        errs = compare_bwd([sl(t.cpu()) for t in (gq, gk, gv)], ref, "bf16", what)
+        _say(what, " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+
+
+def test_backward_rows_without_keys_many_heads():
+    # rows with LSE = -inf (no visible key) in a launch wide enough for 128
+    # keys per dK/dV workgroup: they add nothing to dK, dV
+    Nq, Nkv = 150, 333
+    w = Workload("bwdZ", 2, 256, Nq, 128, "bf16", 9650, tangent_scale=0.1, n_kv=Nkv)
+    x = make_inputs(w)
+    empty = np.array([0, 5, 6, 64, 127, Nq - 1])
+    vis = lambda qi, ki: ~np.isin(qi, empty)[:, None] & np.ones((1, len(ki)), dtype=bool)
+    o64, _, lse64, _ = attention_jvp(*(to_float64(x[n]) for n in NAMES), visible=vis)
+    q, k, v = (x[n].cuda() for n in ("q", "k", "v"))
+    o = torch.from_numpy(o64).to(q.dtype).cuda()
+    lse = torch.from_numpy(lse64).float().cuda()
+    g_cpu = _grad_input(w, w.seed + 1)
+    gq, gk, gv, _ = aj.bwd(q, k, v, o, g_cpu.cuda(), lse)
+    torch.cuda.synchronize()
+    ref = attention_backward(to_float64(x["q"]), to_float64(x["k"]), to_float64(x["v"]),
+                             to_float64(g_cpu), visible=vis)
+    errs = compare_bwd([to_float64(t) for t in (gq, gk, gv)], ref, "bf16",
+                       "bwd rows without keys, 2x256 heads")
+    assert np.all(to_float64(gq)[:, :, empty] == 0.0)
+    _say("bwd rows without keys, 2x256 heads", " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+
+
 def test_backward_strided_bshd_views():
     # inputs and outputs stored [B, N, H, d] and passed as [B, H, N, d] views
     B, H, Nq, Nkv, d = 2, 3, 170, 230, 64
