@@ -80,6 +80,36 @@ def test_text_cross_attention_shape():
     _check(w, what="text Lq4096 Lkv300")
 
 
+@pytest.mark.parametrize("B,H,Nq,Nkv,d", [(2, 23, 4000, 500, 128), (4, 16, 4352, 333, 64)])
+def test_persistent_cross_attention(B, H, Nq, Nkv, d):
+    # short key walks (8 and 6 tiles) over more query blocks than CUs: the
+    # persistent launch, in which a workgroup fetches its next block's first
+    # tile and Q, dQ rows during the current block's last tile.  1,472 blocks
+    # (not a multiple of the 256 workgroups), a ragged last query block and a
+    # ragged key tail; every row against the oracle, and one head alone (a
+    # plain launch of 32 or 23 blocks) gives the same O and LSE bitwise
+    w = Workload("persist", B, H, Nq, d, "bf16", 7300 + d, tangent_scale=0.1, n_kv=Nkv)
+    _say(f"persistent cross-attention B{B} H{H} Lq{Nq} Lkv{Nkv} d{d}")
+    _check(w, what=f"persistent Lq{Nq} Lkv{Nkv} d{d}")
+    x = make_inputs(w)
+    g = {n: x[n].cuda() for n in NAMES}
+    full = aj.fwd(*(g[n] for n in NAMES))
+    b, h = B - 1, H // 2
+    one = aj.fwd(*(g[n][b:b + 1, h:h + 1].contiguous() for n in NAMES))
+    torch.cuda.synchronize()
+    o, do, lse, dlse = (t[b:b + 1, h:h + 1] for t in full)
+    assert torch.equal(o, one[0]) and torch.equal(lse, one[2])
+    # dO and dLSE may differ by where the compiler fuses the multiply-adds of
+    # the tangent row sum r (a sum with cancellation, so its rounding is set
+    # by the size of its terms, not of r): within 1e-6 of max|dLSE|, and a
+    # bf16 ulp of dO
+    dl1 = one[3].double()
+    assert float((dlse.double() - dl1).abs().max()) <= 1e-6 * float(dl1.abs().max())
+    do1 = one[1].double()
+    tol = 2.0 ** -7 * do1.abs() + 1e-6 * float(do1.abs().max())
+    assert bool(((do.double() - do1).abs() <= tol).all())
+
+
 def test_custom_scale_unequal_dims():
     w = Workload("s", 1, 2, 100, 32, "bf16", 7100, tangent_scale=0.3, n_kv=250, d_v=256)
     _check(w, scale=0.5, what="scale dqk32 dv256")
