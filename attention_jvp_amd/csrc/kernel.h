@@ -436,7 +436,16 @@ void attn_jvp_kernel(Params p) {
   static_assert(NSTEP == 1 || NSTEP == 2, "tile shape");
   static_assert(DQK % KI == 0 && DV % 16 == 0, "head dims");
 
-  __shared__ __attribute__((aligned(1024))) char smem[C::kLds];
+  // Output staging (bfloat16, d_qk = d_v >= 64): each wave's 16 rows of O,
+  // then of dO, pass through LDS rows of its own beyond the tile stages, so
+  // that the global stores write whole rows (16 bytes per lane, 1 KiB per
+  // instruction) instead of 32-byte pieces of 16 rows.  Measured with per-
+  // block timestamps, issuing the direct stores took 1.9 us per block.
+  constexpr int kOutRow = DV * (int)sizeof(T);
+  constexpr int kOutWave = kWaveRows * kOutRow;
+  constexpr bool kStageOut =
+      BF16 && DQK == DV && DV >= 64 && C::kLds + W * kOutWave <= 160 * 1024;
+  __shared__ __attribute__((aligned(1024))) char smem[C::kLds + (kStageOut ? W * kOutWave : 0)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -902,6 +911,14 @@ void attn_jvp_kernel(Params p) {
   using NotLast = std::integral_constant<bool, false>;
   // with a next block (ntile even) the last tile, in stage 1, is peeled
   const int body = has_next ? ntile - 2 : ntile;
+  // The key loop's code starts on a 64-byte boundary (the assembler pads
+  // with s_nop here, once per block).  The loop is the same instruction
+  // sequence in every build, but where it lands modulo 32 bytes moved the
+  // time of the 1 x 40 x 32760 d = 128 launch by up to 8 % (49.4 to 53.6 ms
+  // over the eight 4-byte offsets, image-DiT within 0.5 %); pinning it keeps
+  // that from changing with unrelated code ahead of the loop, at the offset
+  // that measured best.
+  asm volatile(".p2align 6");
   int it = 0;
   for (; it + 1 < body; it += 2) {
     tile(S0{}, it, NotLast{});
@@ -939,6 +956,64 @@ void attn_jvp_kernel(Params p) {
     if (lg == 0) {
       p.lse[row] = empty ? -INFINITY : (m_run + log2f(l_tot)) * 0.69314718055994530942f;
       p.dlse[row] = mu;
+    }
+  } else if (kStageOut && !p.partial) {
+    // Lane (qi, lg) puts its 4 values of d block e at row qi, bytes
+    // (16 e + 4 lg) * 2 of the wave's rows; 16-byte chunk c of row r sits at
+    // slot c ^ (r / RPB mod CPR) (RPB rows per 256-byte bank sweep): the
+    // 8-byte writes (16 rows of one chunk per pass) and the 16-byte row reads
+    // are free of bank conflicts.  Lane l then stores 16 bytes: chunk l mod
+    // CPR of row RPI j + l / CPR.
+    if constexpr (kStageOut) {
+      constexpr int CPR = kOutRow / 16, RPB = kOutRow >= 256 ? 1 : 256 / kOutRow;
+      constexpr int RPI = 64 / CPR;
+      static_assert(CPR <= 64 && kWaveRows % RPI == 0, "staged rows");
+      char *ws = smem + C::kLds + wave * kOutWave;
+      typedef T T4 __attribute__((ext_vector_type(4)));
+      typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+      auto slot = [](int r, int c) __attribute__((always_inline)) {
+        return r * kOutRow + ((c ^ ((r / RPB) % CPR)) << 4);
+      };
+      auto put = [&](int e, const T4 &v) __attribute__((always_inline)) {
+        const int bc = (16 * e + 4 * lg) * (int)sizeof(T);
+        *(T4 *)(ws + slot(qi, bc >> 4) + (bc & 15)) = v;
+      };
+      auto store_rows = [&](void *base) __attribute__((always_inline)) {
+        const int row0 = q0 + wave * kWaveRows;
+#pragma unroll
+        for (int j = 0; j < kWaveRows / RPI; ++j) {
+          const int r = RPI * j + lane / CPR, c = lane % CPR;
+          const u32x4 v = *(const u32x4 *)(ws + slot(r, c));
+          if (row0 + r < Nq)
+            *(u32x4 *)((char *)base + ((int64_t)(row0 + r) * p.so[2]) * (int64_t)sizeof(T) + c * 16) = v;
+        }
+      };
+      char *Ob = (char *)((T *)p.o + b * p.so[0] + h * p.so[1]);
+      char *dOb = (char *)((T *)p.dout + b * p.so[0] + h * p.so[1]);
+#pragma unroll
+      for (int e = 0; e < ND; ++e) {
+        T4 ov;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ov[i] = (T)(oacc[e][i] * inv);
+        put(e, ov);
+      }
+      store_rows(Ob);
+#pragma unroll
+      for (int e = 0; e < ND; ++e) {
+        T4 dv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float o = oacc[e][i] * inv;
+          dv[i] = (T)(fmaf(bacc[e][i], sinv, aacc[e][i] * inv) - mu * o);
+        }
+        put(e, dv);
+      }
+      store_rows(dOb);
+      if (qvalid && lg == 0) {
+        const int64_t ro = (int64_t)bh * Nq + qrow;
+        p.lse[ro] = empty ? -INFINITY : (m_run + log2f(l_tot)) * 0.69314718055994530942f;
+        p.dlse[ro] = mu;
+      }
     }
   } else if (qvalid) {
     T *O = (T *)p.o + b * p.so[0] + h * p.so[1] + (int64_t)qrow * p.so[2];
