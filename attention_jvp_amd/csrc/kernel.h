@@ -388,6 +388,50 @@ struct SideCopier {
   }
 };
 
+// Stores of a wave's 16 rows of DV bfloat16 results held in the MFMA layout
+// (lane l holds elements 16 e + 4 (l / 16) + 0..3 of row l % 16) through 16
+// rows of LDS private to the wave: each lane writes its 8-byte pieces, then
+// reads back and stores 16 bytes of a whole row, so that a store instruction
+// writes 4 whole 256-byte rows (d = 128) instead of 32-byte pieces of 16.
+// 16-byte chunk c of row r sits at slot c ^ (r / RPB mod CPR), RPB rows per
+// 256-byte bank sweep: the writes (16 rows of one chunk per pass) and the
+// row reads are free of bank conflicts.  Rows at or past nvalid are not
+// stored.  LDS operations of a wave complete in order, so the same rows can
+// serve the next call at once.
+template <typename T, int DV>
+struct RowStager {
+  static constexpr int kRow = DV * (int)sizeof(T);
+  static constexpr int CPR = kRow / 16;
+  static constexpr int RPB = kRow >= 256 ? 1 : 256 / kRow;
+  static constexpr int RPI = 64 / CPR;   // rows per store instruction
+  static constexpr int kBytes = 16 * kRow;
+  static constexpr bool kBuilt = sizeof(T) == 2 && DV >= 64 && CPR <= 64;
+  typedef T T4 __attribute__((ext_vector_type(4)));
+  typedef unsigned U4 __attribute__((ext_vector_type(4)));
+
+  __device__ static int slot(int r, int c) { return r * kRow + ((c ^ ((r / RPB) % CPR)) << 4); }
+
+  // vals(e): the lane's T4 of 16-wide block e; base: byte address of row 0;
+  // stride: bytes between rows
+  template <typename F>
+  __device__ static void store(char *ws, int lane, F &&vals, char *base, int64_t stride,
+                               int nvalid) {
+    static_assert(kBuilt && 16 % RPI == 0, "row staging");
+    const int rl = lane & 15, lg = lane >> 4;
+#pragma unroll
+    for (int e = 0; e < DV / 16; ++e) {
+      const int bc = (16 * e + 4 * lg) * (int)sizeof(T);
+      *(T4 *)(ws + slot(rl, bc >> 4) + (bc & 15)) = vals(e);
+    }
+#pragma unroll
+    for (int j = 0; j < 16 / RPI; ++j) {
+      const int r = RPI * j + lane / CPR, c = lane % CPR;
+      const U4 v = *(const U4 *)(ws + slot(r, c));
+      if (r < nvalid) *(U4 *)(base + r * stride + c * 16) = v;
+    }
+  }
+};
+
 __device__ inline void wait_vmem() {
   // s_waitcnt vmcnt(0): every global->LDS copy this wave issued has landed
   __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -441,10 +485,10 @@ void attn_jvp_kernel(Params p) {
   // that the global stores write whole rows (16 bytes per lane, 1 KiB per
   // instruction) instead of 32-byte pieces of 16 rows.  Measured with per-
   // block timestamps, issuing the direct stores took 1.9 us per block.
-  constexpr int kOutRow = DV * (int)sizeof(T);
-  constexpr int kOutWave = kWaveRows * kOutRow;
+  using Stager = RowStager<T, DV>;
+  constexpr int kOutWave = Stager::kBytes;
   constexpr bool kStageOut =
-      BF16 && DQK == DV && DV >= 64 && C::kLds + W * kOutWave <= 160 * 1024;
+      Stager::kBuilt && DQK == DV && C::kLds + W * kOutWave <= 160 * 1024;
   __shared__ __attribute__((aligned(1024))) char smem[C::kLds + (kStageOut ? W * kOutWave : 0)];
 
   const int tid = threadIdx.x;
@@ -958,57 +1002,28 @@ void attn_jvp_kernel(Params p) {
       p.dlse[row] = mu;
     }
   } else if (kStageOut && !p.partial) {
-    // Lane (qi, lg) puts its 4 values of d block e at row qi, bytes
-    // (16 e + 4 lg) * 2 of the wave's rows; 16-byte chunk c of row r sits at
-    // slot c ^ (r / RPB mod CPR) (RPB rows per 256-byte bank sweep): the
-    // 8-byte writes (16 rows of one chunk per pass) and the 16-byte row reads
-    // are free of bank conflicts.  Lane l then stores 16 bytes: chunk l mod
-    // CPR of row RPI j + l / CPR.
     if constexpr (kStageOut) {
-      constexpr int CPR = kOutRow / 16, RPB = kOutRow >= 256 ? 1 : 256 / kOutRow;
-      constexpr int RPI = 64 / CPR;
-      static_assert(CPR <= 64 && kWaveRows % RPI == 0, "staged rows");
       char *ws = smem + C::kLds + wave * kOutWave;
-      typedef T T4 __attribute__((ext_vector_type(4)));
-      typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-      auto slot = [](int r, int c) __attribute__((always_inline)) {
-        return r * kOutRow + ((c ^ ((r / RPB) % CPR)) << 4);
-      };
-      auto put = [&](int e, const T4 &v) __attribute__((always_inline)) {
-        const int bc = (16 * e + 4 * lg) * (int)sizeof(T);
-        *(T4 *)(ws + slot(qi, bc >> 4) + (bc & 15)) = v;
-      };
-      auto store_rows = [&](void *base) __attribute__((always_inline)) {
-        const int row0 = q0 + wave * kWaveRows;
+      const int row0 = q0 + wave * kWaveRows;
+      const int64_t stride = p.so[2] * (int64_t)sizeof(T);
+      char *Ob = (char *)((T *)p.o + b * p.so[0] + h * p.so[1]) + row0 * stride;
+      char *dOb = (char *)((T *)p.dout + b * p.so[0] + h * p.so[1]) + row0 * stride;
+      typedef typename Stager::T4 T4;
+      Stager::store(ws, lane, [&](int e) __attribute__((always_inline)) {
+        T4 v;
 #pragma unroll
-        for (int j = 0; j < kWaveRows / RPI; ++j) {
-          const int r = RPI * j + lane / CPR, c = lane % CPR;
-          const u32x4 v = *(const u32x4 *)(ws + slot(r, c));
-          if (row0 + r < Nq)
-            *(u32x4 *)((char *)base + ((int64_t)(row0 + r) * p.so[2]) * (int64_t)sizeof(T) + c * 16) = v;
-        }
-      };
-      char *Ob = (char *)((T *)p.o + b * p.so[0] + h * p.so[1]);
-      char *dOb = (char *)((T *)p.dout + b * p.so[0] + h * p.so[1]);
-#pragma unroll
-      for (int e = 0; e < ND; ++e) {
-        T4 ov;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ov[i] = (T)(oacc[e][i] * inv);
-        put(e, ov);
-      }
-      store_rows(Ob);
-#pragma unroll
-      for (int e = 0; e < ND; ++e) {
-        T4 dv;
+        for (int i = 0; i < 4; ++i) v[i] = (T)(oacc[e][i] * inv);
+        return v;
+      }, Ob, stride, Nq - row0);
+      Stager::store(ws, lane, [&](int e) __attribute__((always_inline)) {
+        T4 v;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float o = oacc[e][i] * inv;
-          dv[i] = (T)(fmaf(bacc[e][i], sinv, aacc[e][i] * inv) - mu * o);
+          v[i] = (T)(fmaf(bacc[e][i], sinv, aacc[e][i] * inv) - mu * o);
         }
-        put(e, dv);
-      }
-      store_rows(dOb);
+        return v;
+      }, dOb, stride, Nq - row0);
       if (qvalid && lg == 0) {
         const int64_t ro = (int64_t)bh * Nq + qrow;
         p.lse[ro] = empty ? -INFINITY : (m_run + log2f(l_tot)) * 0.69314718055994530942f;
