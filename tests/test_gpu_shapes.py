@@ -110,6 +110,27 @@ def test_persistent_cross_attention(B, H, Nq, Nkv, d):
     assert bool(((do.double() - do1).abs() <= tol).all())
 
 
+@pytest.mark.parametrize("B,H,Nq,Nkv,d", [(2, 23, 4000, 500, 128), (1, 3, 333, 333, 128),
+                                           (2, 2, 200, 230, 64)])
+def test_row_stores_into_strided_outputs(B, H, Nq, Nkv, d):
+    # inputs and outputs stored [B, N, H, d] and passed as [B, H, N, d] views
+    # (rows H * d apart): the epilogue's whole-row stores follow the output
+    # strides and skip the rows past Lq; bitwise the same as contiguous
+    # tensors (persistent and plain launches, ragged last query block)
+    w = Workload("rows", B, H, Nq, d, "bf16", 7400 + d + Nq, tangent_scale=0.1, n_kv=Nkv)
+    x = make_inputs(w)
+    flat = aj.fwd(*(x[n].cuda() for n in NAMES))
+    g = {n: x[n].transpose(1, 2).contiguous().cuda().transpose(1, 2) for n in NAMES}
+    o = torch.full((B, Nq, H, d), float("nan"), device="cuda", dtype=torch.bfloat16).transpose(1, 2)
+    do = torch.full_like(o, float("nan"))
+    lse = torch.empty((B, H, Nq), device="cuda")
+    dlse = torch.empty_like(lse)
+    aj.fwd(*(g[n] for n in NAMES), out=(o, do, lse, dlse))
+    torch.cuda.synchronize()
+    for a, c in zip(flat, (o, do, lse, dlse)):
+        assert torch.equal(a, c)
+
+
 def test_custom_scale_unequal_dims():
     w = Workload("s", 1, 2, 100, 32, "bf16", 7100, tangent_scale=0.3, n_kv=250, d_v=256)
     _check(w, scale=0.5, what="scale dqk32 dv256")
