@@ -89,18 +89,20 @@ inline bool fwd_pick_small(int es, int dqk, int dv, int64_t bh, int64_t nq, bool
 #endif
 
 // Persistent forward launches (kernel.h, PERSIST), built for bfloat16
-// d_qk = d_v = 64 and 128.  A workgroup's fixed cost (measured with per-block
-// timestamps at d = 128: about 4.5 us from dispatch to its first key tile,
+// d_qk = d_v = 128 (at d = 64 the twelve-wave instance, held to 168
+// registers, spills with the persistent loop and the row-staged stores).
+// A workgroup's fixed cost (measured with per-block timestamps at d = 128:
+// about 4.5 us from dispatch to its first key tile,
 // 2 us of epilogue, 2.2 us until the CU's next workgroup starts) is paid once
 // per block of a plain launch; a persistent workgroup fetches its next
 // block's first tile and Q, dQ rows during the last tile of the current one.
 // That pays where a block walks few key tiles (3 % at 8 and 16 tiles) and
-// not at the long ones (image-DiT's 64 tiles: the same time; 68 tiles at
-// d = 64: 1 % slower), so it is chosen up to kPersistMaxTiles.
+// not at the long ones (image-DiT's 64 tiles: the same time), so it is
+// chosen up to kPersistMaxTiles.
 constexpr int kPersistMaxTiles = 16;
 
 constexpr bool fwd_has_persist(int es, int dqk, int dv) {
-  return es == 2 && dqk == dv && (dqk == 128 || dqk == 64);
+  return es == 2 && dqk == 128 && dv == 128;
 }
 
 // A persistent launch of `wgs` workgroups (one per CU, a multiple of 8) for

@@ -354,7 +354,7 @@ static void check_splits() {
 
 // Persistent forward launches: p.persist is 0 or the CU count rounded down
 // to a multiple of 8, and it is set only for unmasked bfloat16 launches at
-// d_qk = d_v = 64 or 128 with one key split, outside the small geometry,
+// d_qk = d_v = 128 with one key split, outside the small geometry,
 // whose blocks walk an even number of key tiles (at most kPersistMaxTiles)
 // and outnumber the workgroups.
 static void check_persist() {
@@ -386,7 +386,7 @@ static void check_persist() {
     const int wgs = cus / 8 * 8;
     const int64_t ntile = (nkv + g.block_n - 1) / g.block_n;
     const int64_t blocks = (int64_t)bh * ((nq + g.block_m - 1) / g.block_m);
-    const bool want = dtype == ATTN_JVP_BF16 && (d == 64 || d == 128) && !masked && !sm &&
+    const bool want = dtype == ATTN_JVP_BF16 && d == 128 && !masked && !sm &&
                       wgs >= 8 && ntile % 2 == 0 && ntile <= kPersistMaxTiles && blocks > wgs;
     CHECK(p.persist == (want ? wgs : 0), "persist %d for dtype %d d %d bh %d nq %d nkv %d cus %d",
           p.persist, dtype, d, bh, nq, nkv, cus);
@@ -394,14 +394,14 @@ static void check_persist() {
   }
   CHECK(taken > 0, "a persistent launch never taken");
   // on 256 CUs: cross-attention of 2 x 24 heads x 4096 queries to 512 text
-  // tokens (d = 128) and of 4 x 16 heads x 4352 queries (d = 64, twelve-wave
-  // blocks) to 512 keys are persistent; 4096 keys (64 tiles), 300 keys at
-  // d = 64 (5 tiles), the frame window, and the small geometry of
-  // 2 x 24 x 4096 at d = 64 are not
+  // tokens (d = 128) is persistent; 4096 keys (64 tiles), 500 keys in 2 x 23
+  // heads of 4000 queries (8 tiles) but 4 x 16 x 4352 at d = 64 (no
+  // persistent instance), an odd tile count (400 keys: 7 tiles), and the frame window
+  // are not
   const struct { int b, h, nq, nkv, d, masked, want; } known[6] = {
-      {2, 24, 4096, 512, 128, 0, 256}, {4, 16, 4352, 512, 64, 0, 256},
-      {2, 24, 4096, 4096, 128, 0, 0},  {4, 16, 4352, 300, 64, 0, 0},
-      {2, 24, 4096, 512, 128, 1, 0},   {2, 24, 4096, 512, 64, 0, 0}};
+      {2, 24, 4096, 512, 128, 0, 256}, {2, 23, 4000, 500, 128, 0, 256},
+      {2, 24, 4096, 4096, 128, 0, 0},  {4, 16, 4352, 512, 64, 0, 0},
+      {2, 24, 4096, 400, 128, 0, 0},   {2, 24, 4096, 512, 128, 1, 0}};
   for (const auto &k : known) {
     const attn_jvp_shape sh = {k.b, k.h, k.nq, k.nkv, k.d, k.d};
     const attn_jvp_mask wide = {ATTN_JVP_MASK_FRAME_WINDOW, 64, 64, 2, 1, 1, 1, 0};

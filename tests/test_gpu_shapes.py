@@ -80,14 +80,14 @@ def test_text_cross_attention_shape():
     _check(w, what="text Lq4096 Lkv300")
 
 
-@pytest.mark.parametrize("B,H,Nq,Nkv,d", [(2, 23, 4000, 500, 128), (4, 16, 4352, 333, 64)])
+@pytest.mark.parametrize("B,H,Nq,Nkv,d", [(2, 23, 4000, 500, 128), (2, 23, 4000, 333, 128)])
 def test_persistent_cross_attention(B, H, Nq, Nkv, d):
     # short key walks (8 and 6 tiles) over more query blocks than CUs: the
     # persistent launch, in which a workgroup fetches its next block's first
     # tile and Q, dQ rows during the current block's last tile.  1,472 blocks
     # (not a multiple of the 256 workgroups), a ragged last query block and a
     # ragged key tail; every row against the oracle, and one head alone (a
-    # plain launch of 32 or 23 blocks) gives the same O and LSE bitwise
+    # plain launch of 32 blocks) gives the same O and LSE bitwise
     w = Workload("persist", B, H, Nq, d, "bf16", 7300 + d, tangent_scale=0.1, n_kv=Nkv)
     _say(f"persistent cross-attention B{B} H{H} Lq{Nq} Lkv{Nkv} d{d}")
     _check(w, what=f"persistent Lq{Nq} Lkv{Nkv} d{d}")
