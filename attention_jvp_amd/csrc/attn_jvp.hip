@@ -99,33 +99,6 @@ int scratch_of_stream(hipStream_t stream, void **out) {
   return ATTN_JVP_OK;
 }
 
-// Compute units of the device a launch on `stream` runs on (the current
-// device for the null stream), cached per device; 0 if it cannot be told
-// (the launch then takes the plain grid).
-std::mutex cus_mu;
-int cus_of[kMaxDevices];
-
-int compute_units(hipStream_t stream) {
-  int dev = -1;
-  if (stream) {
-    hipDevice_t sdev = -1;
-    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return 0;
-    dev = (int)sdev;
-  } else if (hipGetDevice(&dev) != hipSuccess) {
-    return 0;
-  }
-  if (dev < 0 || dev >= kMaxDevices) return 0;
-  std::lock_guard<std::mutex> lock(cus_mu);
-  if (!cus_of[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0)
-      return 0;
-    cus_of[dev] = n;
-  }
-  return cus_of[dev];
-}
-
 }  // namespace
 
 using namespace attn_jvp;
@@ -143,8 +116,6 @@ int attn_jvp_fwd_ex(const void *Q, const void *K, const void *V, const void *dQ,
   if (st != ATTN_JVP_OK) return st;
   Params p = make_params(Q, K, V, dQ, dK, dV, O, dO, LSE, dLSE, *shape, scale, dtype, L, mask);
   if (launch_small(*shape, dtype, mask)) set_small(&p, dtype, *shape);
-  if (fwd_has_persist(dtype == ATTN_JVP_BF16 ? 2 : 4, shape->head_dim_qk, shape->head_dim_v))
-    set_persist(&p, dtype, *shape, mask, compute_units((hipStream_t)stream));
   return status_of(dispatch(p, dtype, shape->head_dim_qk, shape->head_dim_v, mask_on(mask),
                             (hipStream_t)stream));
 }

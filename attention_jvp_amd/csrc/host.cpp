@@ -122,20 +122,6 @@ void set_small(Params *p, int dtype, const attn_jvp_shape &s) {
   p->nqb = (p->Nq + g.block_m - 1) / g.block_m;
 }
 
-void set_persist(Params *p, int dtype, const attn_jvp_shape &s, const attn_jvp_mask *mask,
-                 int cus) {
-  p->persist = 0;
-  if (!dtype_ok(dtype)) return;
-  const int es = esize_of(dtype);
-  FwdGeom g;
-  if (!shape_for(dtype, s.head_dim_qk, s.head_dim_v, &g)) return;
-  const int wgs = cus / 8 * 8;
-  const int64_t blocks = (int64_t)p->B * p->H * p->nqb * p->nsplit;
-  if (fwd_pick_persist(es, s.head_dim_qk, s.head_dim_v, blocks, s.seqlen_kv, g.block_n,
-                       mask_on(mask), p->small != 0, p->nsplit, wgs) && !p->partial)
-    p->persist = wgs;
-}
-
 attn_jvp_layout contiguous(const attn_jvp_shape &s) {
   attn_jvp_layout L;
   const int64_t nq = s.seqlen_q, nkv = s.seqlen_kv, dqk = s.head_dim_qk, dv = s.head_dim_v;

@@ -28,10 +28,6 @@ bool shape_for(int dtype, int dqk, int dv, FwdGeom *out);
 // (fwd16_geom_small)?  set_small switches a launch's parameters to it.
 bool launch_small(const attn_jvp_shape &s, int dtype, const attn_jvp_mask *mask);
 void set_small(Params *p, int dtype, const attn_jvp_shape &s);
-// Persistent launch for a device of `cus` compute units (fwd_pick_persist):
-// sets p->persist to the grid size, or leaves it 0.
-void set_persist(Params *p, int dtype, const attn_jvp_shape &s, const attn_jvp_mask *mask,
-                 int cus);
 
 attn_jvp_layout contiguous(const attn_jvp_shape &s);
 attn_jvp_bwd_layout contiguous_bwd(const attn_jvp_shape &s);

@@ -24,10 +24,6 @@ hipError_t launch_pair(const Params &p, bool masked, hipStream_t s) {
     if (p.small) return launch_instance<T, DQK, DV, false, true>(p, s);
   }
   if (p.small) return hipErrorInvalidValue;
-  if constexpr (fwd_has_persist((int)sizeof(T), DQK, DV)) {
-    if (p.persist) return launch_instance<T, DQK, DV, false, false, true>(p, s);
-  }
-  if (p.persist) return hipErrorInvalidValue;
   return launch_instance<T, DQK, DV, false>(p, s);
 }
 

@@ -363,12 +363,6 @@ struct SideCopier {
     }
   }
 
-  // another (b, h) of the same tensors (same row stride)
-  __device__ void rebase(const T *t0, const T *t1) {
-    base[0] = (const char *)t0;
-    base[1] = (const char *)t1;
-  }
-
   // LDS: tensor t of stage g at dst0 + t * tstride (dst0 already holds g)
   __device__ void issue(int k0, int N, char *dst0, int tstride) const {
     const int valid = (N - k0 < BN ? N - k0 : BN) - 1;   // last real row
@@ -450,13 +444,7 @@ __device__ inline void wait_vmem() {
 constexpr float kRescaleThreshold = 8.0f;
 
 // The small geometry runs three workgroups per CU (at most 168 registers).
-// PERSIST (unmasked, one key split, an even number of key tiles): a launch of
-// gridDim.x workgroups (a multiple of 8) in which workgroup w walks the
-// blocks w, w + gridDim.x, ... of the B * H * nqb query blocks; each block's
-// first key tile and Q, dQ rows are fetched during the previous block's last
-// tile, so that neither the workgroup's dispatch nor those fetches stand
-// between two blocks.
-template <typename T, int DQK, int DV, bool MASKED, bool SMALL = false, bool PERSIST = false>
+template <typename T, int DQK, int DV, bool MASKED, bool SMALL = false>
 __global__ __launch_bounds__((Cfg<T, DQK, DV, SMALL>::kThreads), (SMALL ? 3 : 1))
 void attn_jvp_kernel(Params p) {
   using C = Cfg<T, DQK, DV, SMALL>;
@@ -496,16 +484,9 @@ void attn_jvp_kernel(Params p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int qi = lane & 15;        // this lane's query within the wave
   const int lg = lane >> 4;        // lane group 0..3
-  static_assert(!PERSIST || !MASKED, "persistent launches are unmasked");
 
-  // Q, dQ fragments (B operands of S^T = K Q^T), resident for a block
-  FragK qf[DS], dqf[DS];
-  const int nvirt = p.B * p.H * p.nqb * p.nsplit;   // blocks of a persistent launch
-  int vblk = blockIdx.x;
-  bool fetched = false;   // this block's first tile and Q, dQ are in flight
-  for (;;) {   // one iteration per query block (the body keeps its indentation)
   // logical id = (bh * nqb + qb) * nsplit + split
-  const int lid_all = PERSIST ? logical_id_of(vblk, nvirt) : logical_block_id();
+  const int lid_all = logical_block_id();
   const int lid = lid_all / p.nsplit;
   const int split = lid_all - lid * p.nsplit;
   const int bh = lid / p.nqb;
@@ -549,55 +530,24 @@ void attn_jvp_kernel(Params p) {
   auto issue_v = [&](int it, int g) __attribute__((always_inline)) {
     vcopy.issue(tile_at(tr, t_first + it) * BN, Nkv, smem + VB + g * TV, 2 * TV);
   };
-  if (ntile > 0 && !fetched) issue_tile(0, 0);
+  if (ntile > 0) issue_tile(0, 0);
 
   const int qrow = q0 + wave * kWaveRows + qi;
   const bool qvalid = qrow < Nq;
 
-  auto load_q = [&](const T *Qb, const T *dQb, int row) __attribute__((always_inline)) {
+  // ---- Q, dQ fragments (B operands of S^T = K Q^T), resident ----
+  FragK qf[DS], dqf[DS];
 #pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      if (row < Nq) {
-        const int64_t off = (int64_t)row * p.sq[2] + s * KI + lg * KL;
-        qf[s] = *(const FragK *)(Qb + off);
-        dqf[s] = *(const FragK *)(dQb + off);
-      } else {
-        qf[s] = FragK{};
-        dqf[s] = FragK{};
-      }
+  for (int s = 0; s < DS; ++s) {
+    if (qvalid) {
+      const int64_t off = (int64_t)qrow * p.sq[2] + s * KI + lg * KL;
+      qf[s] = *(const FragK *)(Q + off);
+      dqf[s] = *(const FragK *)(dQ + off);
+    } else {
+      qf[s] = FragK{};
+      dqf[s] = FragK{};
     }
-  };
-  if (!fetched) load_q(Q, dQ, qrow);
-
-  // Persistent launches: the next block of this workgroup.  Its first tile
-  // goes to stage 0 while the last tile of this block (stage 1: ntile even)
-  // is in use, its K, dK behind this tile's first scores and V, dV behind the
-  // second; its Q, dQ rows go into qf, dqf once this tile's last scores have
-  // read them.
-  const int vnext = vblk + (int)gridDim.x;
-  const bool has_next = PERSIST && vnext < nvirt && ntile > 0 && ntile % 2 == 0;
-  int b_n = 0, h_n = 0, q0_n = 0;
-  if (has_next) {
-    const int lid_n = logical_id_of(vnext, nvirt);
-    const int bh_n = lid_n / p.nqb;
-    q0_n = (lid_n - bh_n * p.nqb) * C::kBlockM;
-    b_n = bh_n / p.H;
-    h_n = bh_n - b_n * p.H;
   }
-  auto prefetch_k = [&](int g) __attribute__((always_inline)) {
-    kcopy.rebase((const T *)p.k + b_n * p.sk[0] + h_n * p.sk[1],
-                 (const T *)p.dk + b_n * p.sk[0] + h_n * p.sk[1]);
-    kcopy.issue(0, Nkv, smem + g * TK, 2 * TK);
-  };
-  auto prefetch_v = [&](int g) __attribute__((always_inline)) {
-    vcopy.rebase((const T *)p.v + b_n * p.sv[0] + h_n * p.sv[1],
-                 (const T *)p.dv + b_n * p.sv[0] + h_n * p.sv[1]);
-    vcopy.issue(0, Nkv, smem + VB + g * TV, 2 * TV);
-  };
-  auto prefetch_q = [&]() __attribute__((always_inline)) {
-    load_q((const T *)p.q + b_n * p.sq[0] + h_n * p.sq[1],
-           (const T *)p.dq + b_n * p.sq[0] + h_n * p.sq[1], q0_n + wave * kWaveRows + qi);
-  };
 
   // O^T, A^T = (P~ dV)^T and B^T = ((P~ . dS) V)^T blocks (dS without the
   // scale, applied once in the epilogue): lane holds d = 16e + 4 lg + 0..3 of
@@ -896,10 +846,7 @@ void attn_jvp_kernel(Params p) {
     body();
     if constexpr (kOverlap) __builtin_amdgcn_s_setprio(0);
   };
-  // LAST_: the block's last tile of a persistent launch with a next block
-  // (which it fetches); every other tile fetches the next of its block.
-  auto tile = [&](auto G_, int it, auto LAST_) __attribute__((always_inline)) {
-    constexpr bool LAST = decltype(LAST_)::value;
+  auto tile = [&](auto G_, int it) __attribute__((always_inline)) {
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
     const int k0 = tile_at(tr, t_first + it) * BN;
@@ -912,36 +859,30 @@ void attn_jvp_kernel(Params p) {
     // first scores, V and dV after the second step's scores where the order
     // overlaps), not at the barrier where every wave would issue them while
     // the matrix cores idle
-    if constexpr (LAST) prefetch_k(1 - decltype(G_)::value);
-    else if (it + 1 < ntile) issue_k(it + 1, 1 - decltype(G_)::value);
+    if (it + 1 < ntile) issue_k(it + 1, 1 - decltype(G_)::value);
     if constexpr (!kOverlap) {
-      if constexpr (LAST) prefetch_v(1 - decltype(G_)::value);
-      else if (it + 1 < ntile) issue_v(it + 1, 1 - decltype(G_)::value);
+      if (it + 1 < ntile) issue_v(it + 1, 1 - decltype(G_)::value);
     }
     if (need) apply_mask(k0, sa, dsa);
     update_max(sa);
     if constexpr (NSTEP == 1) {
-      if constexpr (LAST) prefetch_q();
       softmax(sa, dsa);
       mfma_block([&]() __attribute__((always_inline)) { accumulate(G_, C0{}, sa, dsa); });
     } else {
       f32x4 sb[2], dsb[2];
       if constexpr (kOverlap) {
         mfma_block([&]() __attribute__((always_inline)) { scores(G_, C1{}, sb, dsb); });
-        if constexpr (LAST) prefetch_q();
         softmax(sa, dsa);
         // the exponentials of a are computed here, beside the scores of b,
         // not sunk past the mask branch below
         asm volatile("" ::"v"(sa[0]), "v"(sa[1]), "v"(dsa[0]), "v"(dsa[1]));
-        if constexpr (LAST) prefetch_v(1 - decltype(G_)::value);
-        else if (it + 1 < ntile) issue_v(it + 1, 1 - decltype(G_)::value);
+        if (it + 1 < ntile) issue_v(it + 1, 1 - decltype(G_)::value);
         if (need) apply_mask(k0 + CK, sb, dsb);
         mfma_block([&]() __attribute__((always_inline)) { accumulate(G_, C0{}, sa, dsa); });
       } else {
         softmax(sa, dsa);
         mfma_block([&]() __attribute__((always_inline)) { accumulate(G_, C0{}, sa, dsa); });
         mfma_block([&]() __attribute__((always_inline)) { scores(G_, C1{}, sb, dsb); });
-        if constexpr (LAST) prefetch_q();
         if (need) apply_mask(k0 + CK, sb, dsb);
       }
       update_max(sb);
@@ -950,28 +891,21 @@ void attn_jvp_kernel(Params p) {
     }
   };
 
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  using NotLast = std::integral_constant<bool, false>;
-  // with a next block (ntile even) the last tile, in stage 1, is peeled
-  const int body = has_next ? ntile - 2 : ntile;
-  // The key loop's code starts on a 64-byte boundary (the assembler pads
-  // with s_nop here, once per block).  The loop is the same instruction
-  // sequence in every build, but where it lands modulo 32 bytes moved the
-  // time of the 1 x 40 x 32760 d = 128 launch by up to 8 % (49.4 to 53.6 ms
-  // over the eight 4-byte offsets, image-DiT within 0.5 %); pinning it keeps
-  // that from changing with unrelated code ahead of the loop, at the offset
-  // that measured best.
-  asm volatile(".p2align 6");
+  // The key loop's code starts 20 bytes past a 64-byte boundary (the
+  // assembler pads with s_nop here, once per block).  Where the same loop
+  // lands modulo 32 bytes moved the time of the 1 x 40 x 32760 d = 128
+  // launch by up to 9 % (47.9 to 52.5 ms over the eight 4-byte offsets of
+  // this loop; image-DiT 0.929 to 0.943 ms); pinning it keeps that from
+  // changing with unrelated code ahead of the loop, at the offset that
+  // measured best.  A change to the loop's own code calls for measuring the
+  // offsets again.
+  asm volatile(".p2align 6\n s_nop 0\n s_nop 0\n s_nop 0\n s_nop 0\n s_nop 0");
   int it = 0;
-  for (; it + 1 < body; it += 2) {
-    tile(S0{}, it, NotLast{});
-    tile(S1{}, it + 1, NotLast{});
+  for (; it + 1 < ntile; it += 2) {
+    tile(std::integral_constant<int, 0>{}, it);
+    tile(std::integral_constant<int, 1>{}, it + 1);
   }
-  if (it < ntile) tile(S0{}, it, NotLast{});
-  if constexpr (PERSIST) {
-    if (has_next) tile(S1{}, it + 1, std::integral_constant<bool, true>{});
-  }
+  if (it < ntile) tile(std::integral_constant<int, 0>{}, it);
 
   // ---- epilogue ----
   const float l_tot = row_sum4(l_run);
@@ -1055,24 +989,15 @@ void attn_jvp_kernel(Params p) {
       p.dlse[ro] = mu;
     }
   }
-  if constexpr (!PERSIST) {
-    break;
-  } else {
-    if (vnext >= nvirt) break;
-    fetched = has_next;
-    vblk = vnext;
-  }
-  }  // blocks of a persistent launch
 }
 
-// Launch one instance: grid = B * H * ceil(Nq / block_m) * nsplit workgroups
-// (p.persist workgroups for a persistent instance).
-template <typename T, int DQK, int DV, bool MASKED, bool SMALL = false, bool PERSIST = false>
+// Launch one instance: grid = B * H * ceil(Nq / block_m) * nsplit workgroups.
+template <typename T, int DQK, int DV, bool MASKED, bool SMALL = false>
 hipError_t launch_instance(const Params &p, hipStream_t stream) {
   using C = Cfg<T, DQK, DV, SMALL>;
-  const int grid = PERSIST ? p.persist : p.B * p.H * p.nqb * p.nsplit;
-  hipLaunchKernelGGL((attn_jvp_kernel<T, DQK, DV, MASKED, SMALL, PERSIST>), dim3(grid),
-                     dim3(C::kThreads), 0, stream, p);
+  const int grid = p.B * p.H * p.nqb * p.nsplit;
+  hipLaunchKernelGGL((attn_jvp_kernel<T, DQK, DV, MASKED, SMALL>), dim3(grid), dim3(C::kThreads),
+                     0, stream, p);
   return hipGetLastError();
 }
 

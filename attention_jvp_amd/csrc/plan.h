@@ -88,34 +88,6 @@ inline bool fwd_pick_small(int es, int dqk, int dv, int64_t bh, int64_t nq, bool
 #define ATTN_JVP_ROWS32_D64 0
 #endif
 
-// Persistent forward launches (kernel.h, PERSIST), built for bfloat16
-// d_qk = d_v = 128 (at d = 64 the twelve-wave instance, held to 168
-// registers, spills with the persistent loop and the row-staged stores).
-// A workgroup's fixed cost (measured with per-block timestamps at d = 128:
-// about 4.5 us from dispatch to its first key tile,
-// 2 us of epilogue, 2.2 us until the CU's next workgroup starts) is paid once
-// per block of a plain launch; a persistent workgroup fetches its next
-// block's first tile and Q, dQ rows during the last tile of the current one.
-// That pays where a block walks few key tiles (3 % at 8 and 16 tiles) and
-// not at the long ones (image-DiT's 64 tiles: the same time), so it is
-// chosen up to kPersistMaxTiles.
-constexpr int kPersistMaxTiles = 16;
-
-constexpr bool fwd_has_persist(int es, int dqk, int dv) {
-  return es == 2 && dqk == 128 && dv == 128;
-}
-
-// A persistent launch of `wgs` workgroups (one per CU, a multiple of 8) for
-// an unmasked launch with one key split: when the blocks take more than one
-// round and every block walks an even number of key tiles, at most
-// kPersistMaxTiles.
-inline bool fwd_pick_persist(int es, int dqk, int dv, int64_t blocks, int nkv, int block_n,
-                             bool masked, bool small, int nsplit, int wgs) {
-  if (!fwd_has_persist(es, dqk, dv) || masked || small || nsplit != 1 || wgs < 8) return false;
-  const int64_t ntile = (nkv + (int64_t)block_n - 1) / block_n;
-  return ntile % 2 == 0 && ntile <= kPersistMaxTiles && blocks > wgs;
-}
-
 constexpr bool use_rows32(int es, int dqk, int dv) {
   return es == 2 && dqk == dv &&
          ((dqk == 128 && ATTN_JVP_ROWS32_D128) || (dqk == 64 && ATTN_JVP_ROWS32_D64));
@@ -297,7 +269,6 @@ struct Params {
   int nsplit;                           // key splits per query block (1: none)
   int partial;                          // 1: outputs are float32 partials
   int small;                            // 1: the small geometry (fwd16_geom_small)
-  int persist;                          // > 0: persistent launch of this many workgroups
   float scale, scale_log2;
   MaskDev mask;
 };

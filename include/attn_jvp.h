@@ -43,11 +43,10 @@
  *   - The call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream).  Arguments are validated on the host before anything is
  *     launched; on error nothing is launched and a negative status returns.
- *   - No C++ exception crosses this interface.  Apart from per-device
- *     constants cached on first use (a device's compute-unit count, which
- *     sizes persistent forward launches; the static scratch address of the
- *     allocation-free entry point), the library keeps no state between
- *     calls, and it is safe to call from several host threads.
+ *   - No C++ exception crosses this interface.  Apart from the static
+ *     scratch address of the allocation-free entry point, cached per device
+ *     on first use, the library keeps no state between calls, and it is
+ *     safe to call from several host threads.
  *   - Calls that run concurrently on one device race only if their outputs
  *     overlap.
  */

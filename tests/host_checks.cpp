@@ -15,7 +15,6 @@
 //     sizes up to the limits of the types: every call returns a status, the
 //     launch-size limits hold, and a set of known-bad calls is rejected.
 //  3. Split planning: choose_splits and split_workspace over many shapes.
-//  4. The choice of persistent forward launches (set_persist).
 //
 // Prints "host checks: ok" and exits 0, or prints the first failure and
 // exits 1.
@@ -352,74 +351,10 @@ static void check_splits() {
   CHECK(ns >= 1 && ns <= 64, "masked splits %d", ns);
 }
 
-// Persistent forward launches: p.persist is 0 or the CU count rounded down
-// to a multiple of 8, and it is set only for unmasked bfloat16 launches at
-// d_qk = d_v = 128 with one key split, outside the small geometry,
-// whose blocks walk an even number of key tiles (at most kPersistMaxTiles)
-// and outnumber the workgroups.
-static void check_persist() {
-  const attn_jvp_mask fw = {ATTN_JVP_MASK_FRAME_WINDOW, 4, 64, 2, 1, 1, 1, 0};
-  const int cus_set[6] = {0, 7, 8, 80, 256, 304};
-  const int dims[5] = {16, 32, 64, 128, 256};
-  char buf[64];
-  float fb[4];
-  uint64_t y = 0x13198a2e03707344ull;
-  int taken = 0;
-  for (int i = 0; i < 20000; ++i) {
-    y ^= y << 13;
-    y ^= y >> 7;
-    y ^= y << 17;
-    const int d = dims[y % 5], dtype = (int)((y >> 8) % 2), cus = cus_set[(y >> 12) % 6];
-    const bool masked = ((y >> 60) & 3) == 0;   // the window holds 256 tokens
-    const int bh = 1 + (int)((y >> 16) % 512);
-    const int nq = masked ? 256 : 1 + (int)((y >> 28) % 9000);
-    const int nkv = masked ? 256 : 1 + (int)((y >> 42) % 3000);
-    const attn_jvp_shape sh = {1, bh, nq, nkv, d, d};
-    if (!fwd_built(dtype == ATTN_JVP_BF16 ? 2 : 4, d, d)) continue;
-    const attn_jvp_mask *m = masked ? &fw : nullptr;
-    const attn_jvp_layout L = contiguous(sh);
-    Params p = make_params(buf, buf, buf, buf, buf, buf, buf, buf, fb, fb, sh, 0.f, dtype, L, m);
-    const bool sm = launch_small(sh, dtype, m);
-    if (sm) set_small(&p, dtype, sh);
-    set_persist(&p, dtype, sh, m, cus);
-    const FwdGeom g = sm ? fwd16_geom_small(2, 64, 64) : fwd_geom(dtype == ATTN_JVP_BF16 ? 2 : 4, d, d);
-    const int wgs = cus / 8 * 8;
-    const int64_t ntile = (nkv + g.block_n - 1) / g.block_n;
-    const int64_t blocks = (int64_t)bh * ((nq + g.block_m - 1) / g.block_m);
-    const bool want = dtype == ATTN_JVP_BF16 && d == 128 && !masked && !sm &&
-                      wgs >= 8 && ntile % 2 == 0 && ntile <= kPersistMaxTiles && blocks > wgs;
-    CHECK(p.persist == (want ? wgs : 0), "persist %d for dtype %d d %d bh %d nq %d nkv %d cus %d",
-          p.persist, dtype, d, bh, nq, nkv, cus);
-    taken += p.persist != 0;
-  }
-  CHECK(taken > 0, "a persistent launch never taken");
-  // on 256 CUs: cross-attention of 2 x 24 heads x 4096 queries to 512 text
-  // tokens (d = 128) is persistent; 4096 keys (64 tiles), 500 keys in 2 x 23
-  // heads of 4000 queries (8 tiles) but 4 x 16 x 4352 at d = 64 (no
-  // persistent instance), an odd tile count (400 keys: 7 tiles), and the frame window
-  // are not
-  const struct { int b, h, nq, nkv, d, masked, want; } known[6] = {
-      {2, 24, 4096, 512, 128, 0, 256}, {2, 23, 4000, 500, 128, 0, 256},
-      {2, 24, 4096, 4096, 128, 0, 0},  {4, 16, 4352, 512, 64, 0, 0},
-      {2, 24, 4096, 400, 128, 0, 0},   {2, 24, 4096, 512, 128, 1, 0}};
-  for (const auto &k : known) {
-    const attn_jvp_shape sh = {k.b, k.h, k.nq, k.nkv, k.d, k.d};
-    const attn_jvp_mask wide = {ATTN_JVP_MASK_FRAME_WINDOW, 64, 64, 2, 1, 1, 1, 0};
-    const attn_jvp_mask *m = k.masked ? &wide : nullptr;
-    Params p = make_params(buf, buf, buf, buf, buf, buf, buf, buf, fb, fb, sh, 0.f,
-                           ATTN_JVP_BF16, contiguous(sh), m);
-    if (launch_small(sh, ATTN_JVP_BF16, m)) set_small(&p, ATTN_JVP_BF16, sh);
-    set_persist(&p, ATTN_JVP_BF16, sh, m, 256);
-    CHECK(p.persist == k.want, "persist %d, expected %d (%d x %d x %d x %d, d %d, mask %d)",
-          p.persist, k.want, k.b, k.h, k.nq, k.nkv, k.d, k.masked);
-  }
-}
-
 int main() {
   check_work_lists();
   check_validation();
   check_splits();
-  check_persist();
   if (failures) {
     printf("host checks: %d failures\n", failures);
     return 1;

@@ -80,34 +80,23 @@ def test_text_cross_attention_shape():
     _check(w, what="text Lq4096 Lkv300")
 
 
-@pytest.mark.parametrize("B,H,Nq,Nkv,d", [(2, 23, 4000, 500, 128), (2, 23, 4000, 333, 128)])
-def test_persistent_cross_attention(B, H, Nq, Nkv, d):
-    # short key walks (8 and 6 tiles) over more query blocks than CUs: the
-    # persistent launch, in which a workgroup fetches its next block's first
-    # tile and Q, dQ rows during the current block's last tile.  1,472 blocks
-    # (not a multiple of the 256 workgroups), a ragged last query block and a
-    # ragged key tail; every row against the oracle, and one head alone (a
-    # plain launch of 32 blocks) gives the same O and LSE bitwise
-    w = Workload("persist", B, H, Nq, d, "bf16", 7300 + d, tangent_scale=0.1, n_kv=Nkv)
-    _say(f"persistent cross-attention B{B} H{H} Lq{Nq} Lkv{Nkv} d{d}")
-    _check(w, what=f"persistent Lq{Nq} Lkv{Nkv} d{d}")
+@pytest.mark.parametrize("B,H,Nq,Nkv,d", [(2, 23, 4000, 500, 128), (4, 16, 4352, 333, 64)])
+def test_cross_attention_many_blocks(B, H, Nq, Nkv, d):
+    # short key walks (8 and 6 tiles) over more query blocks than CUs: 1,472
+    # blocks, a ragged last query block and a ragged key tail; every row
+    # against the oracle, and one head alone (a launch of 32 or 23 blocks)
+    # gives the same outputs bitwise
+    w = Workload("xblocks", B, H, Nq, d, "bf16", 7300 + d, tangent_scale=0.1, n_kv=Nkv)
+    _say(f"cross-attention B{B} H{H} Lq{Nq} Lkv{Nkv} d{d}")
+    _check(w, what=f"cross Lq{Nq} Lkv{Nkv} d{d}")
     x = make_inputs(w)
     g = {n: x[n].cuda() for n in NAMES}
     full = aj.fwd(*(g[n] for n in NAMES))
     b, h = B - 1, H // 2
     one = aj.fwd(*(g[n][b:b + 1, h:h + 1].contiguous() for n in NAMES))
     torch.cuda.synchronize()
-    o, do, lse, dlse = (t[b:b + 1, h:h + 1] for t in full)
-    assert torch.equal(o, one[0]) and torch.equal(lse, one[2])
-    # dO and dLSE may differ by where the compiler fuses the multiply-adds of
-    # the tangent row sum r (a sum with cancellation, so its rounding is set
-    # by the size of its terms, not of r): within 1e-6 of max|dLSE|, and a
-    # bf16 ulp of dO
-    dl1 = one[3].double()
-    assert float((dlse.double() - dl1).abs().max()) <= 1e-6 * float(dl1.abs().max())
-    do1 = one[1].double()
-    tol = 2.0 ** -7 * do1.abs() + 1e-6 * float(do1.abs().max())
-    assert bool(((do.double() - do1).abs() <= tol).all())
+    for a, c in zip(full, one):
+        assert torch.equal(a[b:b + 1, h:h + 1], c)
 
 
 @pytest.mark.parametrize("B,H,Nq,Nkv,d", [(2, 23, 4000, 500, 128), (1, 3, 333, 333, 128),
@@ -116,7 +105,7 @@ def test_row_stores_into_strided_outputs(B, H, Nq, Nkv, d):
     # inputs and outputs stored [B, N, H, d] and passed as [B, H, N, d] views
     # (rows H * d apart): the epilogue's whole-row stores follow the output
     # strides and skip the rows past Lq; bitwise the same as contiguous
-    # tensors (persistent and plain launches, ragged last query block)
+    # tensors (many blocks and few, ragged last query block)
     w = Workload("rows", B, H, Nq, d, "bf16", 7400 + d + Nq, tangent_scale=0.1, n_kv=Nkv)
     x = make_inputs(w)
     flat = aj.fwd(*(x[n].cuda() for n in NAMES))
