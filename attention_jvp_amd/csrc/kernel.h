@@ -891,15 +891,17 @@ void attn_jvp_kernel(Params p) {
     }
   };
 
-  // The key loop's code starts 20 bytes past a 64-byte boundary (the
-  // assembler pads with s_nop here, once per block).  Where the same loop
-  // lands modulo 32 bytes moved the time of the 1 x 40 x 32760 d = 128
-  // launch by up to 9 % (47.9 to 52.5 ms over the eight 4-byte offsets of
-  // this loop; image-DiT 0.929 to 0.943 ms); pinning it keeps that from
+  // The key loop's code starts 20 bytes past a 64-byte boundary (8 bytes
+  // for the twelve-wave d = 64 instance; the assembler pads with s_nop here,
+  // once per block).  Where the same loop lands modulo 32 bytes moved the
+  // time of the 1 x 40 x 32760 d = 128 launch by up to 9 % (47.9 to 52.5 ms
+  // over the eight 4-byte offsets of this loop; image-DiT 0.929 to 0.943 ms;
+  // text-to-image at d = 64 0.746 to 0.754 ms); pinning it keeps that from
   // changing with unrelated code ahead of the loop, at the offset that
   // measured best.  A change to the loop's own code calls for measuring the
   // offsets again.
-  asm volatile(".p2align 6\n s_nop 0\n s_nop 0\n s_nop 0\n s_nop 0\n s_nop 0");
+  if constexpr (DQK == 64 && !SMALL) asm volatile(".p2align 6\n s_nop 0\n s_nop 0");
+  else asm volatile(".p2align 6\n s_nop 0\n s_nop 0\n s_nop 0\n s_nop 0\n s_nop 0");
   int it = 0;
   for (; it + 1 < ntile; it += 2) {
     tile(std::integral_constant<int, 0>{}, it);
