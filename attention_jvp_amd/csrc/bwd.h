@@ -469,7 +469,7 @@ void bwd_kernel(BwdParams p) {
         constexpr int kb2 = j / DS, s = j % DS;
         if constexpr (j + PD - 1 < NP) issue(std::integral_constant<int, j + PD - 1>{});
         constexpr int newer = (NP - 1 - j) < (PD - 1) ? (NP - 1 - j) : (PD - 1);
-        lds_pair_wait<2 * newer>(r0f[j], r1f[j]);
+        lds_wait<2 * newer>();
 #pragma unroll
         for (int rb = 0; rb < R; ++rb) {
           x_[rb][kb2] = EK::mfma(r0f[j], af[rb][s], x_[rb][kb2]);
@@ -600,11 +600,11 @@ void bwd_kernel(BwdParams p) {
         i16x4(&cur)[4] = buf[e % 3];
         if constexpr (e + 2 < ND) {
           issue(std::integral_constant<int, e + 2>{}, buf[(e + 2) % 3]);
-          lds_tr_wait<2 * NR>(cur[0], cur[1], cur[2], cur[3]);
+          lds_wait<2 * NR>();
         } else if constexpr (e + 1 < ND) {
-          lds_tr_wait<NR>(cur[0], cur[1], cur[2], cur[3]);
+          lds_wait<NR>();
         } else {
-          lds_tr_wait<0>(cur[0], cur[1], cur[2], cur[3]);
+          lds_wait<0>();
         }
         const FragV t0f = __builtin_bit_cast(FragV, __builtin_shufflevector(cur[0], cur[1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll

@@ -249,7 +249,7 @@ __device__ inline int lds_off(int r, int byte_col) {
 // touch the LDS stage an in-flight global->LDS copy is filling, and would
 // otherwise wait for every outstanding copy (vmcnt(0)) before the first one,
 // serialising the tile prefetch.  The compiler does not count these reads, so
-// lds_tr_wait() must run before their results are used; extra LDS operations
+// lds_wait() must run before their results are used; extra LDS operations
 // it does not know about only make its own lgkmcnt waits stronger, since LDS
 // operations complete in issue order.
 template <int OFF>
@@ -273,18 +273,24 @@ __device__ __attribute__((always_inline)) inline void static_for(F &&f) {
   }
 }
 
-// Wait until at most N LDS operations are outstanding; the four values pass
-// through the asm so that nothing reading them can be scheduled before it.
+// Wait until at most N LDS operations are outstanding (the asm-issued reads
+// above and below included), then a scheduling barrier that no instruction
+// crosses, so that nothing reading their values is scheduled before the
+// wait.  Tying the values through an asm wait instead (an output operand per
+// value) orders them as well, but the compiler then takes the asm for the
+// values' last VALU writer and puts a wait state (s_nop) between it and the
+// MFMA that reads them next: five to eight more s_nop per 32-key step of the
+// d = 128 forward, which measured 2-3 % slower there and in the backward.
 template <int N>
-__device__ inline void lds_tr_wait(i16x4 &a, i16x4 &b, i16x4 &c, i16x4 &d) {
+__device__ inline void lds_wait() {
   static_assert(N >= 0 && N <= 15, "lgkmcnt field");
-  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "n"(N));
+  // vmcnt 63 and expcnt 7 (no wait on either), lgkmcnt N
+  __builtin_amdgcn_s_waitcnt(0xC07F | (N << 8));
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // K-side operand read (one 16-byte row slice of K or dK), issued through
-// inline asm for the reason given at lds_read_tr; lds_pair_wait<N> waits
-// until at most N LDS operations are outstanding and passes the two values
-// through the asm, so that no MFMA reading them is scheduled before it.
+// inline asm for the reason given at lds_read_tr; lds_wait<N> waits for it.
 // Holding the reads in flight this way lets the score MFMAs of one slice
 // run while the next slices are still on their way from LDS.
 template <int OFF>
@@ -293,12 +299,6 @@ __device__ inline bf16x8 lds_read_k(uint32_t addr) {
   bf16x8 v;
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
   return v;
-}
-
-template <int N>
-__device__ inline void lds_pair_wait(bf16x8 &a, bf16x8 &b) {
-  static_assert(N >= 0 && N <= 15, "lgkmcnt field");
-  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
 }
 
 // Sum and maximum over the four lanes l, l^16, l^32, l^48 that hold one
@@ -645,7 +645,7 @@ void attn_jvp_kernel(Params p) {
         constexpr int kb2 = j / DS, s = j % DS;
         if constexpr (j + PD - 1 < NP) issue(std::integral_constant<int, j + PD - 1>{});
         constexpr int newer = (NP - 1 - j) < (PD - 1) ? (NP - 1 - j) : (PD - 1);
-        lds_pair_wait<2 * newer>(kf[j], dkf[j]);
+        lds_wait<2 * newer>();
         s_[kb2] = EK::mfma(kf[j], qf[s], s_[kb2]);
         ds_[kb2] = EK::mfma(kf[j], dqf[s], ds_[kb2]);
         ds_[kb2] = EK::mfma(dkf[j], qf[s], ds_[kb2]);
@@ -781,11 +781,11 @@ void attn_jvp_kernel(Params p) {
         i16x4(&cur)[4] = buf[e % 3];
         if constexpr (e + 2 < ND) {
           issue(std::integral_constant<int, e + 2>{}, buf[(e + 2) % 3]);
-          lds_tr_wait<8>(cur[0], cur[1], cur[2], cur[3]);
+          lds_wait<8>();
         } else if constexpr (e + 1 < ND) {
-          lds_tr_wait<4>(cur[0], cur[1], cur[2], cur[3]);
+          lds_wait<4>();
         } else {
-          lds_tr_wait<0>(cur[0], cur[1], cur[2], cur[3]);
+          lds_wait<0>();
         }
         const FragV vf = __builtin_bit_cast(FragV, __builtin_shufflevector(cur[0], cur[1], 0, 1, 2, 3, 4, 5, 6, 7));
         const FragV dvf = __builtin_bit_cast(FragV, __builtin_shufflevector(cur[2], cur[3], 0, 1, 2, 3, 4, 5, 6, 7));
@@ -891,17 +891,15 @@ void attn_jvp_kernel(Params p) {
     }
   };
 
-  // The key loop's code starts 20 bytes past a 64-byte boundary (8 bytes
-  // for the twelve-wave d = 64 instance; the assembler pads with s_nop here,
-  // once per block).  Where the same loop lands modulo 32 bytes moved the
-  // time of the 1 x 40 x 32760 d = 128 launch by up to 9 % (47.9 to 52.5 ms
-  // over the eight 4-byte offsets of this loop; image-DiT 0.929 to 0.943 ms;
-  // text-to-image at d = 64 0.746 to 0.754 ms); pinning it keeps that from
-  // changing with unrelated code ahead of the loop, at the offset that
-  // measured best.  A change to the loop's own code calls for measuring the
-  // offsets again.
-  if constexpr (DQK == 64 && !SMALL) asm volatile(".p2align 6\n s_nop 0\n s_nop 0");
-  else asm volatile(".p2align 6\n s_nop 0\n s_nop 0\n s_nop 0\n s_nop 0\n s_nop 0");
+  // The key loop's code starts on a 64-byte boundary (the assembler pads
+  // with s_nop here, once per block).  Where the same loop lands modulo 32
+  // bytes moved the time of the 1 x 40 x 32760 d = 128 launch by up to 9 %
+  // (over the eight 4-byte offsets of this loop: 47.3 to 52.7 ms; image-DiT
+  // 0.918 to 0.950 ms; text-to-image at d = 64 0.768 to 0.781 ms); pinning
+  // it keeps that from changing with unrelated code ahead of the loop, at
+  // the offset that measured best.  A change to the loop's own code calls
+  // for measuring the offsets again.
+  asm volatile(".p2align 6");
   int it = 0;
   for (; it + 1 < ntile; it += 2) {
     tile(std::integral_constant<int, 0>{}, it);

@@ -312,7 +312,7 @@ __global__ __launch_bounds__(Cfg32<D>::kThreads, Cfg32<D>::kMinBlocks) void attn
       constexpr int s = decltype(s_)::value;
       if constexpr (s + PD - 1 < NSL) kread(g, kf, dkf, std::integral_constant<int, s + PD - 1>{});
       constexpr int newer = (NSL - 1 - s) < (PD - 1) ? (NSL - 1 - s) : (PD - 1);
-      lds_pair_wait<2 * newer>(kf[s], dkf[s]);
+      lds_wait<2 * newer>();
       mfma32_scores<s == 0>(S, dS, kf[s], dkf[s], qf[s], dqf[s]);
       between(s_);
       __builtin_amdgcn_sched_barrier(0);
@@ -346,7 +346,7 @@ __global__ __launch_bounds__(Cfg32<D>::kThreads, Cfg32<D>::kMinBlocks) void attn
       if constexpr (v + VD - 1 < NV)
         issue(std::integral_constant<int, v + VD - 1>{}, buf[(v + VD - 1) % VD]);
       constexpr int newer = (NV - 1 - v) < (VD - 1) ? (NV - 1 - v) : (VD - 1);
-      lds_tr_wait<4 * newer>(cur[0], cur[1], cur[2], cur[3]);
+      lds_wait<4 * newer>();
       const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(cur[0], cur[1], 0, 1, 2, 3, 4, 5, 6, 7));
       const bf16x8 dvf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(cur[2], cur[3], 0, 1, 2, 3, 4, 5, 6, 7));
       mfma32_values(oacc[e], aacc[e], bacc[e], vf, dvf, P[kk], H[kk]);
