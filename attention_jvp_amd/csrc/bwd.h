@@ -208,7 +208,7 @@ void bwd_kernel(BwdParams p) {
   const int r_hi = r0 + W * R * kWaveRows < Nown ? r0 + W * R * kWaveRows : Nown;
 
   // streamed tiles this block visits, in ascending order (all of them
-  // without a mask); iteration it walks tile tile_at(tr, it)
+  // without a mask); iteration it walks tile walk_at(walk, it)
   TileRanges tr;
   if constexpr (MASKED) {
     tr = KEYS ? visible_query_tiles(p.mask, r0, r_hi, Nq, BN)
@@ -217,6 +217,7 @@ void bwd_kernel(BwdParams p) {
     tr = all_tiles(Nstr, BN);
   }
   const int ntile = tile_count(tr);
+  const TileWalk walk = tile_walk(tr);
 
   // Mask terms.  The lane's own row sees the streamed rows [vis_lo, vis_hi)
   // by the chunk rule, plus [0, a_first_hi) and [a_last_lo, Nstr) (anchor
@@ -295,7 +296,7 @@ void bwd_kernel(BwdParams p) {
   const uint32_t rows_a = lds_addr(smem) + C::kLds;
   auto issue_rows = [&](int it) __attribute__((always_inline)) {
     if constexpr (KEYS) {
-      int qr = tile_at(tr, it) * BN + lane;
+      int qr = walk_at(walk, it) * BN + lane;
       qr = qr < Nq ? qr : Nq - 1;
       const int which = wave < 2 ? wave : 2;
       const float *src = (which == 1 ? DEL : LSE) + qr;
@@ -310,7 +311,7 @@ void bwd_kernel(BwdParams p) {
         const uint32_t a = rows_a + (it % 3) * kRowSlot + wave * 256 + lane * 4;
         float v;
         asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a));
-        const int qr = tile_at(tr, it) * BN + lane;
+        const int qr = walk_at(walk, it) * BN + lane;
         float t;
         if (wave == 0) t = (qr < Nq && v != -INFINITY) ? -v * kLog2e : -INFINITY;
         else t = -v;
@@ -319,7 +320,7 @@ void bwd_kernel(BwdParams p) {
     }
   };
   auto issue_tile = [&](int it, int g) __attribute__((always_inline)) {
-    copier.issue(tile_at(tr, it) * BN, Nstr, smem + g * TL, 2 * TL);
+    copier.issue(walk_at(walk, it) * BN, Nstr, smem + g * TL, 2 * TL);
   };
   if (ntile > 0) {
     issue_tile(0, 0);
@@ -645,7 +646,7 @@ void bwd_kernel(BwdParams p) {
     wait_vmem();
     __syncthreads();   // tile `it` landed; every wave is done with tile it-1
     const uint32_t rows = rows_a + (it % 3) * kRowSlot;
-    const int t0 = tile_at(tr, it) * BN;
+    const int t0 = walk_at(walk, it) * BN;
     const bool tail = t0 + BN > Nstr;
     const bool need = needs_mask(t0);
     // the next tile's copies (and the query-term rows) go out behind the

@@ -511,6 +511,7 @@ void attn_jvp_kernel(Params p) {
   const int t_first = split * per_split;
   const int t_last = t_first + per_split < nvis ? t_first + per_split : nvis;
   const int ntile = t_last > t_first ? t_last - t_first : 0;
+  const TileWalk walk = tile_walk(tr);
 
   // first tile in flight before anything else
   SideCopier<T, RBK, BN, W, KSK> kcopy;
@@ -520,15 +521,15 @@ void attn_jvp_kernel(Params p) {
   vcopy.init((const T *)p.v + b * p.sv[0] + h * p.sv[1],
              (const T *)p.dv + b * p.sv[0] + h * p.sv[1], p.sv[2], wave, lane);
   auto issue_tile = [&](int it, int g) __attribute__((always_inline)) {
-    const int k0 = tile_at(tr, t_first + it) * BN;
+    const int k0 = walk_at(walk, t_first + it) * BN;
     kcopy.issue(k0, Nkv, smem + g * TK, 2 * TK);
     vcopy.issue(k0, Nkv, smem + VB + g * TV, 2 * TV);
   };
   auto issue_k = [&](int it, int g) __attribute__((always_inline)) {
-    kcopy.issue(tile_at(tr, t_first + it) * BN, Nkv, smem + g * TK, 2 * TK);
+    kcopy.issue(walk_at(walk, t_first + it) * BN, Nkv, smem + g * TK, 2 * TK);
   };
   auto issue_v = [&](int it, int g) __attribute__((always_inline)) {
-    vcopy.issue(tile_at(tr, t_first + it) * BN, Nkv, smem + VB + g * TV, 2 * TV);
+    vcopy.issue(walk_at(walk, t_first + it) * BN, Nkv, smem + VB + g * TV, 2 * TV);
   };
   if (ntile > 0) issue_tile(0, 0);
 
@@ -698,6 +699,11 @@ void attn_jvp_kernel(Params p) {
   // ---- running max (log2 domain) and lazy rescale of the accumulators ----
   // IEEE maximum (NaN-propagating): v_maximum3_f32, no canonicalisation
   constexpr bool kOverlap = BF16 && NSTEP == 2 && DQK + DV >= 256;
+  // s_nop words between the 64-byte boundary and the key loop (see the
+  // loop): the masked bf16 d = 128 loop measured best four words in
+  // (long video 42.7 ms, against 44.8 at the boundary and 42.7-44.0 at the
+  // other offsets), every other instance on the boundary
+  constexpr int kLoopPad = (MASKED && BF16 && DQK == 128 && DV == 128) ? 4 : 0;
   constexpr bool kLaneCheck = !kOverlap && (W >= 8 || SMALL);   // two or more waves per SIMD
   auto update_max = [&](const f32x4 (&sacc)[2]) __attribute__((always_inline)) {
     // eight scores in a tree of three-input maxima
@@ -849,7 +855,7 @@ void attn_jvp_kernel(Params p) {
   auto tile = [&](auto G_, int it) __attribute__((always_inline)) {
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
-    const int k0 = tile_at(tr, t_first + it) * BN;
+    const int k0 = walk_at(walk, t_first + it) * BN;
     const bool need = needs_mask(k0);
     wait_vmem();
     __syncthreads();   // tile `it` landed; every wave is done with tile it-1
@@ -891,15 +897,16 @@ void attn_jvp_kernel(Params p) {
     }
   };
 
-  // The key loop's code starts on a 64-byte boundary (the assembler pads
-  // with s_nop here, once per block).  Where the same loop lands modulo 32
-  // bytes moved the time of the 1 x 40 x 32760 d = 128 launch by up to 9 %
-  // (over the eight 4-byte offsets of this loop: 47.3 to 52.7 ms; image-DiT
-  // 0.918 to 0.950 ms; text-to-image at d = 64 0.768 to 0.781 ms); pinning
-  // it keeps that from changing with unrelated code ahead of the loop, at
-  // the offset that measured best.  A change to the loop's own code calls
-  // for measuring the offsets again.
-  asm volatile(".p2align 6");
+  // The key loop's code starts kLoopPad 4-byte words past a 64-byte
+  // boundary (the assembler pads with s_nop here, once per block).  Where
+  // the same loop lands modulo 32 bytes moved the time of the 1 x 40 x 32760
+  // d = 128 launch by up to 9 % (over the eight 4-byte offsets of this loop:
+  // 47.3 to 52.7 ms; image-DiT 0.918 to 0.950 ms; text-to-image at d = 64
+  // 0.768 to 0.781 ms) and that of the masked long-video launch by 5 %;
+  // pinning it keeps that from changing with unrelated code ahead of the
+  // loop, at the offset that measured best.  A change to the loop's own
+  // code calls for measuring the offsets again.
+  asm volatile(".p2align 6\n\t.rept %0\n\ts_nop 0\n\t.endr" ::"n"(kLoopPad));
   int it = 0;
   for (; it + 1 < ntile; it += 2) {
     tile(std::integral_constant<int, 0>{}, it);

@@ -8,6 +8,7 @@
 
 #pragma once
 
+#include <limits.h>
 #include <stdint.h>
 
 #if defined(__HIPCC__)
@@ -247,14 +248,36 @@ AJ_HD inline int tile_count(const TileRanges &tr) {
   return (tr.hi[0] - tr.lo[0]) + (tr.hi[1] - tr.lo[1]) + (tr.hi[2] - tr.lo[2]);
 }
 
-AJ_HD inline int tile_at(const TileRanges &tr, int idx) {
-  int t = tr.lo[0] + idx;
-  if (tr.n > 1 && t >= tr.hi[0]) {
-    t = tr.lo[1] + (t - tr.hi[0]);
-    if (tr.n > 2 && t >= tr.hi[1]) t = tr.lo[2] + (t - tr.hi[1]);
-  }
+// A walk over the ranges with the steps over the gaps precomputed: the
+// idx-th tile (0 <= idx < tile_count) is base + idx, plus d0 once idx >= j0
+// (range 1 reached) and d1 once idx >= j1 (range 2 reached); a range that
+// does not exist has its j at INT_MAX.  Per tile that is two compares and
+// selects of uniform values (no branches in the key loops); for the one
+// range of an unmasked walk the steps fold away.
+struct TileWalk {
+  int base, j0, d0, j1, d1;
+};
+
+AJ_HD inline TileWalk tile_walk(const TileRanges &tr) {
+  const int len0 = tr.hi[0] - tr.lo[0];
+  const int len01 = len0 + (tr.hi[1] - tr.lo[1]);
+  TileWalk w;
+  w.base = tr.lo[0];
+  w.j0 = tr.n > 1 ? len0 : INT_MAX;
+  w.d0 = tr.n > 1 ? tr.lo[1] - tr.hi[0] : 0;
+  w.j1 = tr.n > 2 ? len01 : INT_MAX;
+  w.d1 = tr.n > 2 ? tr.lo[2] - tr.hi[1] : 0;
+  return w;
+}
+
+AJ_HD inline int walk_at(const TileWalk &w, int idx) {
+  int t = w.base + idx;
+  t += idx >= w.j0 ? w.d0 : 0;
+  t += idx >= w.j1 ? w.d1 : 0;
   return t;
 }
+
+AJ_HD inline int tile_at(const TileRanges &tr, int idx) { return walk_at(tile_walk(tr), idx); }
 
 // ---------------------------------------------------------------------------
 // Kernel parameter blocks.
