@@ -15,6 +15,9 @@
 //     sizes up to the limits of the types: every call returns a status, the
 //     launch-size limits hold, and a set of known-bad calls is rejected.
 //  3. Split planning: choose_splits and split_workspace over many shapes.
+//  4. The tile walk: for random sets of up to three ascending disjoint
+//     ranges (empty ones included), tile_walk / walk_at give, for every
+//     index below tile_count, the tiles of the ranges in ascending order.
 //
 // Prints "host checks: ok" and exits 0, or prints the first failure and
 // exits 1.
@@ -351,7 +354,40 @@ static void check_splits() {
   CHECK(ns >= 1 && ns <= 64, "masked splits %d", ns);
 }
 
+static void check_walks() {
+  uint32_t s = 12345u;
+  auto rnd = [&](int n) {
+    s = s * 1664525u + 1013904223u;
+    return (int)((s >> 8) % (uint32_t)n);
+  };
+  for (int trial = 0; trial < 20000; ++trial) {
+    TileRanges tr;
+    tr.n = 1 + rnd(3);
+    int at = rnd(5);
+    for (int r = 0; r < 3; ++r) {
+      if (r < tr.n) {
+        tr.lo[r] = at;
+        tr.hi[r] = at + (rnd(4) == 0 ? 0 : 1 + rnd(40));   // some ranges empty
+        at = tr.hi[r] + rnd(30);
+      } else {
+        tr.lo[r] = tr.hi[r] = 0;   // unused ranges are empty
+      }
+    }
+    std::vector<int> want;
+    for (int r = 0; r < tr.n; ++r)
+      for (int t = tr.lo[r]; t < tr.hi[r]; ++t) want.push_back(t);
+    CHECK((int)want.size() == tile_count(tr), "walk: tile_count %d, %zu tiles", tile_count(tr),
+          want.size());
+    const TileWalk w = tile_walk(tr);
+    for (int i = 0; i < (int)want.size(); ++i)
+      CHECK(walk_at(w, i) == want[i] && tile_at(tr, i) == want[i],
+            "walk: n %d ranges [%d,%d) [%d,%d) [%d,%d) index %d: %d, want %d", tr.n, tr.lo[0],
+            tr.hi[0], tr.lo[1], tr.hi[1], tr.lo[2], tr.hi[2], i, walk_at(w, i), want[i]);
+  }
+}
+
 int main() {
+  check_walks();
   check_work_lists();
   check_validation();
   check_splits();
