@@ -293,6 +293,23 @@ def test_nan_in_one_key_reaches_exactly_the_rows_that_see_it(tensor):
     _compare(keep, keep_ref, "bf16", f"NaN in one key of {tensor}")
 
 
+@pytest.mark.parametrize("dtype,d,F,T", [("bf16", 128, 7, 150), ("bf16", 64, 5, 333),
+                                         ("fp32", 64, 3, 100)])
+def test_all_visible_window_equals_dense_bitwise(dtype, d, F, T):
+    # a frame window whose chunk spans every frame hides nothing: the masked
+    # kernel instance walks the same key tiles in the same order (one range,
+    # no element masks but the key tail's) and must give the dense
+    # instance's outputs bit for bit
+    mask = dict(frames=F, tokens_per_frame=T, chunk_frames=F, radius_chunks=0,
+                anchor_first=1, anchor_last=1, anchor_queries_see_all=0)
+    w = Workload("allvis", 2, 3, F * T, d, dtype, 18 + d + F, tangent_scale=0.1)
+    _say(f"all-visible window {dtype} d{d} N{F * T}")
+    x = make_inputs(w)
+    dense, masked = _run(x), _run(x, mask=mask)
+    for a, b in zip(dense, masked):
+        assert torch.equal(a, b)
+
+
 def test_zero_score_tangent_matches_output_with_dv_bitwise():
     # dQ = dK = 0: the tangent accumulator sums exactly the products the
     # output accumulator sums when V is replaced by dV
