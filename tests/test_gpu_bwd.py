@@ -264,6 +264,27 @@ def test_backward_deterministic():
         assert torch.equal(s, t)
 
 
+@pytest.mark.parametrize("dtype,d,F,T", [("bf16", 128, 7, 150), ("bf16", 64, 5, 333),
+                                         ("fp32", 32, 3, 100)])
+def test_backward_all_visible_window_equals_dense_bitwise(dtype, d, F, T):
+    # a frame window that hides nothing: both masked launches walk every
+    # streamed tile in the dense order with no element masks, so the
+    # gradients equal the dense launches' bit for bit
+    mask = dict(frames=F, tokens_per_frame=T, chunk_frames=F, radius_chunks=0,
+                anchor_first=1, anchor_last=1, anchor_queries_see_all=0)
+    w = Workload("bwdallvis", 2, 3, F * T, d, dtype, 9600 + d + F, tangent_scale=0.1)
+    _say(f"bwd all-visible window {dtype} d{d} N{F * T}")
+    x = make_inputs(w)
+    q, k, v = (x[n].cuda() for n in ("q", "k", "v"))
+    o, _, lse, _ = aj.fwd(*(x[n].cuda() for n in NAMES))
+    go = _grad_input(w, 7).cuda()
+    dense = aj.bwd(q, k, v, o, go, lse)
+    masked = aj.bwd(q, k, v, o, go, lse, mask=mask)
+    torch.cuda.synchronize()
+    for s, t in zip(dense, masked):
+        assert torch.equal(s, t)
+
+
 def test_backward_errors_launch_nothing():
     w = Workload("bwde", 1, 1, 64, 64, "bf16", 9500, n_kv=64, d_v=32)
     x = make_inputs(w)
